@@ -1,0 +1,162 @@
+/*
+ * muonbank.h -- C ABI of libmuonbank.so, the MI355X (gfx950) Muon bank step.
+ *
+ * The step follows the modded-nanogpt record walkthroughs:
+ *   - banks: stacked parameters viewed zero-copy as [batch, rows, cols]
+ *     ("Unified zero-copy optimizer and transposed LM head", section 1.1);
+ *   - momentum and Nesterov lerps, eff_lr / eff_wd ("Muon Custom Sizing",
+ *     section 4);
+ *   - five quintic Newton-Schulz rounds with coefficients 3.4445, -4.7750,
+ *     2.0315 after a norm scaling ("Muon Custom Sizing", section 2.3;
+ *     GPT-2 Medium Record 7 walkthrough, section 4.2);
+ *   - the mixed-precision apply on bf16 weights plus a uint16 low mantissa
+ *     (Record 7 walkthrough, section 4.1).
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer, owned by the caller; tensors
+ *     are dense and row-major.  The library keeps no pointer after returning.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     All work is enqueued on it; no entry point synchronizes the host.
+ *   - The library never allocates device memory on these paths: scratch
+ *     comes from the caller's `workspace`, sized by the *_workspace_bytes
+ *     queries.  Concurrent calls are safe on distinct workspaces.
+ *   - Errors are return codes (mb_status).  Every argument is validated
+ *     before anything is enqueued: on any status other than MB_OK nothing
+ *     was launched and no buffer changed, except MB_ERR_HIP, which reports
+ *     a failed launch (detail in mb_last_error()).  Faults inside kernels
+ *     surface at the caller's next synchronization, as with any HIP work.
+ *   - Device pointers must be 16-byte aligned (MB_ERR_ALIGN otherwise).
+ *   - Results are deterministic: repeated calls on the same inputs give the
+ *     same bits (fixed reduction orders, no atomics in value paths).
+ */
+#ifndef MUONBANK_H
+#define MUONBANK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MB_OK = 0,
+    MB_ERR_NULL = 1,       /* a required pointer is NULL                                   */
+    MB_ERR_SHAPE = 2,      /* batch/rows/cols <= 0, or the element count overflows          */
+    MB_ERR_DTYPE = 3,      /* unknown dtype code                                            */
+    MB_ERR_ALIGN = 4,      /* a device pointer is not 16-byte aligned                       */
+    MB_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than the matching query returns     */
+    MB_ERR_ALIAS = 6,      /* two buffers overlap where they must not                       */
+    MB_ERR_VALUE = 7,      /* a scalar argument is out of its domain (non-finite, steps<0) */
+    MB_ERR_HIP = 8         /* the HIP runtime rejected a launch                             */
+} mb_status;
+
+typedef enum { MB_F32 = 0, MB_BF16 = 1 } mb_dtype;
+
+/* Hyper-parameters shared by every bank of one call.  Host scalars are taken
+ * in double and rounded once to float32 on the host:
+ *   mu = RN32(momentum), nu = RN32(1 - momentum),
+ *   decay = RN32(1 - lr*weight_decay*wd_mul)               (left to right),
+ *   eta   = RN32(lr*sqrt(max(1, rows/cols))*lr_mul)        (left to right),
+ * the shape-scaled learning rate and decoupled weight decay of "Muon Custom
+ * Sizing", section 4.  Defaults (mb_default_hparams) are Muon's constructor
+ * defaults lr=0.02, weight_decay=0.01, momentum=0.95 (same page, section 2.2)
+ * and the five-round quintic a, b, c = 3.4445, -4.7750, 2.0315 (section 2.3),
+ * eps = 1e-7 in the norm scaling X / (||X||_F + eps). */
+typedef struct {
+    double lr;
+    double weight_decay;
+    double momentum;
+    int32_t ns_steps;
+    double a, b, c;
+    double eps;
+} mb_hparams;
+
+/* One viewed bank [batch, rows, cols] (e.g. attention QKVO (10, 3072, 768)
+ * viewed as (40, 768, 768); MLP (12, 2, 3072, 768) as (24, 3072, 768)).
+ * Slots whose gradient and momentum are all zero (padding, dead layers)
+ * stay exactly zero and their Newton-Schulz work is skipped. */
+typedef struct {
+    int64_t batch, rows, cols;
+    int32_t grad_dtype;              /* MB_F32 or MB_BF16; momentum has the same dtype          */
+    double lr_mul, wd_mul;           /* per-parameter multipliers (1.0 = none)                  */
+    const void *grad;                /* [batch, rows, cols], read only                          */
+    void *momentum;                  /* [batch, rows, cols], updated in place                   */
+    uint16_t *w_hi;                  /* bf16 weight bits (high half of the fp32 master), in place */
+    uint16_t *w_lo;                  /* uint16 low mantissa (low half), in place                */
+    const float *lr_mul_per_slot;    /* optional [batch] float32: eta_slot = RN32(eta*m[i])     */
+    uint16_t *v_out;                 /* optional [batch, rows, cols] bf16: the Newton-Schulz output */
+    uint16_t *u_out;                 /* optional [batch, rows, cols] bf16: the Nesterov update u  */
+} mb_bank;
+
+void mb_default_hparams(mb_hparams *hp);
+const char *mb_status_string(int32_t status);
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char *mb_last_error(void);
+/* Library version string. */
+const char *mb_version(void);
+
+/* Workspace bytes needed by muon_bank_step for these banks (0 on invalid shapes). */
+size_t mb_step_workspace_bytes(const mb_bank *banks, int32_t num_banks);
+/* Workspace bytes needed by ns_orthogonalize_batched for this shape (0 on invalid shapes). */
+size_t mb_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols);
+
+/* The full Muon step on `num_banks` banks, enqueued on one stream:
+ *   1. buf' = RN_M(mu*buf + nu*g) and u = RN_bf16(nu*g + mu*buf'), each
+ *      correctly rounded from the exact value (M = the momentum dtype);
+ *   2. v = NS(u): per slot, on X = u (u^T when rows > cols), X /= ||X||_F + eps,
+ *      then ns_steps times A = X X^T, B = b*A + c*A A, X = a*X + B X;
+ *      bf16 operands on MFMA with fp32 accumulation; A, B, X rounded to bf16
+ *      (round-to-nearest-even) between contractions;
+ *   3. w = fp32(w_hi << 16 | w_lo); t = RN32(w*decay); r = RN32(t - eta_slot*v)
+ *      (one fused multiply-add); w_hi = r >> 16, w_lo = r & 0xFFFF.
+ * Banks must not overlap each other.  hp NULL = defaults. */
+mb_status muon_bank_step(const mb_bank *banks, int32_t num_banks, const mb_hparams *hp,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* Stage 1 alone (momentum + Nesterov): grad, momentum as in mb_bank, u_out
+ * [batch, rows, cols] bf16.  mu and nu are the float32 coefficients
+ * (normally RN32(momentum) and RN32(1 - momentum)).  No workspace. */
+mb_status muon_momentum_update(const void *grad, void *momentum, uint16_t *u_out,
+                               int64_t batch, int64_t rows, int64_t cols, int32_t dtype,
+                               float mu, float nu, void *stream);
+
+/* Stage 2 alone: y = NS(x) for x, y [batch, rows, cols] bf16 (y may equal x
+ * exactly; partial overlap is MB_ERR_ALIAS).  Same arithmetic as stage 2 of
+ * muon_bank_step, with `steps` rounds of (a, b, c) and the given eps. */
+mb_status ns_orthogonalize_batched(const uint16_t *x, uint16_t *y,
+                                   int64_t batch, int64_t rows, int64_t cols,
+                                   int32_t steps, double a, double b, double c, double eps,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Stage 3 alone (Record 7 walkthrough, section 4.1): on every element of
+ * [batch, slot_numel], w = fp32(w_hi << 16 | w_lo); t = RN32(w*decay);
+ * r = RN32(t - eta_slot*v) with one fused multiply-add, eta_slot = eff_lr or,
+ * with lr_mul_per_slot, RN32(eff_lr*lr_mul_per_slot[i]); then w_hi = r >> 16,
+ * w_lo = r & 0xFFFF (a bit slice).  eff_lr and decay are float32, already
+ * rounded.  v is bf16 bits.  No workspace. */
+mb_status mp_apply_update(uint16_t *w_hi, uint16_t *w_lo, const uint16_t *v,
+                          int64_t batch, int64_t slot_numel, float eff_lr, float decay,
+                          const float *lr_mul_per_slot, void *stream);
+
+/* Kernel timing (off by default).  While enabled, every kernel the library
+ * launches is bracketed by two hipEvents on its stream; mb_timing_read waits
+ * for them and returns, per kernel name, the launch count and the summed
+ * duration in milliseconds.  Enabling or reading allocates host-side event
+ * objects only; it does not change any result. */
+typedef struct {
+    char name[48];
+    int64_t launches;
+    double total_ms;
+} mb_kernel_time;
+
+void mb_timing_enable(int32_t on);
+/* Fills up to max_entries records, returns how many kinds were recorded (or
+ * -1 on a HIP error), and clears the recorded events. */
+int32_t mb_timing_read(mb_kernel_time *out, int32_t max_entries);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUONBANK_H */

@@ -1,0 +1,270 @@
+"""Python binding of libmuonbank.so: argument marshalling only.
+
+Each function here has the name of the C entry point it calls (declared in
+``include/muonbank.h``) and does nothing but check that tensors are dense
+device tensors of the right element size, pass their pointers and the current
+HIP stream, and turn a non-OK status into ``MuonBankError``.  All arithmetic
+runs in the library's HIP kernels; there is no fallback.
+
+bf16 bit tensors (weights ``w_hi``, Newton-Schulz input/output, u, v) may be
+``torch.bfloat16``, ``torch.int16`` or ``torch.uint16`` -- only the 2-byte
+storage matters.  The low mantissa ``w_lo`` is any 2-byte integer tensor.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmuonbank.so")
+
+MB_F32, MB_BF16 = 0, 1
+_STATUS = {0: "MB_OK", 1: "MB_ERR_NULL", 2: "MB_ERR_SHAPE", 3: "MB_ERR_DTYPE", 4: "MB_ERR_ALIGN",
+           5: "MB_ERR_WORKSPACE", 6: "MB_ERR_ALIAS", 7: "MB_ERR_VALUE", 8: "MB_ERR_HIP"}
+
+
+class MuonBankError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        self.status_name = _STATUS.get(status, str(status))
+        super().__init__(f"{self.status_name}: {message}")
+
+
+class mb_hparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("weight_decay", ctypes.c_double), ("momentum", ctypes.c_double),
+                ("ns_steps", ctypes.c_int32), ("a", ctypes.c_double), ("b", ctypes.c_double),
+                ("c", ctypes.c_double), ("eps", ctypes.c_double)]
+
+
+class mb_bank(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("grad_dtype", ctypes.c_int32), ("lr_mul", ctypes.c_double), ("wd_mul", ctypes.c_double),
+                ("grad", ctypes.c_void_p), ("momentum", ctypes.c_void_p), ("w_hi", ctypes.c_void_p),
+                ("w_lo", ctypes.c_void_p), ("lr_mul_per_slot", ctypes.c_void_p), ("v_out", ctypes.c_void_p),
+                ("u_out", ctypes.c_void_p)]
+
+
+class mb_kernel_time(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
+
+
+_lib = None
+
+EXPORTED = ("mb_default_hparams", "mb_status_string", "mb_last_error", "mb_version", "mb_step_workspace_bytes",
+            "mb_ns_workspace_bytes", "muon_bank_step", "muon_momentum_update", "ns_orthogonalize_batched",
+            "mp_apply_update", "mb_timing_enable", "mb_timing_read")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmuonbank.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m newton_schulz_bank_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, f64, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                                  ctypes.c_double, ctypes.c_size_t)
+    sig = {
+        "mb_default_hparams": (None, [ctypes.POINTER(mb_hparams)]),
+        "mb_status_string": (ctypes.c_char_p, [i32]),
+        "mb_last_error": (ctypes.c_char_p, []),
+        "mb_version": (ctypes.c_char_p, []),
+        "mb_step_workspace_bytes": (sz, [ctypes.POINTER(mb_bank), i32]),
+        "mb_ns_workspace_bytes": (sz, [i64, i64, i64]),
+        "muon_bank_step": (i32, [ctypes.POINTER(mb_bank), i32, ctypes.POINTER(mb_hparams), vp, sz, vp]),
+        "muon_momentum_update": (i32, [vp, vp, vp, i64, i64, i64, i32, f32, f32, vp]),
+        "ns_orthogonalize_batched": (i32, [vp, vp, i64, i64, i64, i32, f64, f64, f64, f64, vp, sz, vp]),
+        "mp_apply_update": (i32, [vp, vp, vp, i64, i64, f32, f32, vp, vp]),
+        "mb_timing_enable": (None, [i32]),
+        "mb_timing_read": (i32, [ctypes.POINTER(mb_kernel_time), i32]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise MuonBankError(status, lib().mb_last_error().decode())
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dense(t: torch.Tensor, name: str, elem_size: int | tuple = 2) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    sizes = elem_size if isinstance(elem_size, tuple) else (elem_size,)
+    if t.element_size() not in sizes:
+        raise ValueError(f"{name} must have {sizes}-byte elements")
+
+
+def default_hparams() -> mb_hparams:
+    hp = mb_hparams()
+    lib().mb_default_hparams(ctypes.byref(hp))
+    return hp
+
+
+def make_hparams(**kw) -> mb_hparams:
+    hp = default_hparams()
+    for k, v in kw.items():
+        if not hasattr(hp, k):
+            raise KeyError(k)
+        setattr(hp, k, v)
+    return hp
+
+
+@dataclass
+class Bank:
+    """One viewed bank [batch, rows, cols] of device tensors."""
+    grad: torch.Tensor            # bf16 or fp32
+    momentum: torch.Tensor        # same dtype as grad
+    w_hi: torch.Tensor            # bf16 weight (2-byte)
+    w_lo: torch.Tensor            # uint16 low mantissa (2-byte)
+    lr_mul: float = 1.0
+    wd_mul: float = 1.0
+    lr_mul_per_slot: torch.Tensor | None = None   # float32 [batch]
+    v_out: torch.Tensor | None = None             # optional bf16 [batch, rows, cols]
+    u_out: torch.Tensor | None = None             # optional bf16 [batch, rows, cols]
+
+    def to_c(self) -> mb_bank:
+        g = self.grad
+        _dense(g, "grad", (2, 4))
+        if g.dim() != 3:
+            raise ValueError("grad must be [batch, rows, cols]")
+        if g.dtype == torch.float32:
+            dt = MB_F32
+        elif g.dtype == torch.bfloat16:
+            dt = MB_BF16
+        else:
+            raise ValueError("grad must be float32 or bfloat16")
+        if self.momentum.dtype != g.dtype:
+            raise ValueError("momentum must have the gradient's dtype")
+        for name in ("momentum", "w_hi", "w_lo", "v_out", "u_out"):
+            t = getattr(self, name)
+            if t is None:
+                continue
+            _dense(t, name, g.element_size() if name == "momentum" else 2)
+            if tuple(t.shape) != tuple(g.shape):
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(g.shape)}")
+        if self.lr_mul_per_slot is not None:
+            _dense(self.lr_mul_per_slot, "lr_mul_per_slot", 4)
+            if self.lr_mul_per_slot.dtype != torch.float32 or self.lr_mul_per_slot.numel() != g.shape[0]:
+                raise ValueError("lr_mul_per_slot must be float32 [batch]")
+        b, r, c = g.shape
+        return mb_bank(b, r, c, dt, float(self.lr_mul), float(self.wd_mul), _ptr(g), _ptr(self.momentum),
+                       _ptr(self.w_hi), _ptr(self.w_lo), _ptr(self.lr_mul_per_slot), _ptr(self.v_out),
+                       _ptr(self.u_out))
+
+
+def mb_step_workspace_bytes(banks) -> int:
+    arr = (mb_bank * len(banks))(*[b.to_c() for b in banks])
+    return int(lib().mb_step_workspace_bytes(arr, len(banks)))
+
+
+def mb_ns_workspace_bytes(batch: int, rows: int, cols: int) -> int:
+    return int(lib().mb_ns_workspace_bytes(batch, rows, cols))
+
+
+def _workspace(nbytes: int, like: torch.Tensor, workspace: torch.Tensor | None) -> torch.Tensor:
+    if workspace is None:
+        return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=like.device)
+    _dense(workspace, "workspace", (1, 2, 4, 8))
+    return workspace
+
+
+def muon_bank_step(banks, hp: mb_hparams | None = None, workspace: torch.Tensor | None = None, stream=None):
+    """The full Muon step on a list of ``Bank``s (in place on momentum, w_hi, w_lo)."""
+    if isinstance(banks, Bank):
+        banks = [banks]
+    cbanks = [b.to_c() for b in banks]
+    arr = (mb_bank * len(cbanks))(*cbanks)
+    need = int(lib().mb_step_workspace_bytes(arr, len(cbanks)))
+    ws = _workspace(need, banks[0].grad, workspace)
+    hp_ref = ctypes.byref(hp) if hp is not None else None
+    _check(lib().muon_bank_step(arr, len(cbanks), hp_ref, ws.data_ptr(), ws.numel() * ws.element_size(),
+                                _stream(stream)))
+    return ws
+
+
+def muon_momentum_update(grad: torch.Tensor, momentum: torch.Tensor, u_out: torch.Tensor, mu: float, nu: float,
+                         stream=None) -> None:
+    """buf' = RN(mu*buf + nu*g) in place and u = RN_bf16(nu*g + mu*buf') into u_out."""
+    _dense(grad, "grad", (2, 4))
+    _dense(momentum, "momentum", grad.element_size())
+    _dense(u_out, "u_out", 2)
+    if grad.dtype not in (torch.float32, torch.bfloat16) or momentum.dtype != grad.dtype:
+        raise ValueError("grad/momentum must both be float32 or both bfloat16")
+    if grad.dim() != 3 or momentum.shape != grad.shape or u_out.shape != grad.shape:
+        raise ValueError("grad, momentum and u_out must be [batch, rows, cols] of one shape")
+    b, r, c = grad.shape
+    dt = MB_F32 if grad.dtype == torch.float32 else MB_BF16
+    _check(lib().muon_momentum_update(_ptr(grad), _ptr(momentum), _ptr(u_out), b, r, c, dt, float(mu), float(nu),
+                                      _stream(stream)))
+
+
+def ns_orthogonalize_batched(x: torch.Tensor, y: torch.Tensor | None = None, steps: int = 5, a: float = 3.4445,
+                             b: float = -4.7750, c: float = 2.0315, eps: float = 1e-7,
+                             workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y = NS(x) for bf16 [batch, rows, cols]; returns y (a new tensor if none is given)."""
+    _dense(x, "x", 2)
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, rows, cols]")
+    if y is None:
+        y = torch.empty_like(x)
+    _dense(y, "y", 2)
+    if y.shape != x.shape:
+        raise ValueError("y must have x's shape")
+    bt, r, cc = x.shape
+    ws = _workspace(int(lib().mb_ns_workspace_bytes(bt, r, cc)), x, workspace)
+    _check(lib().ns_orthogonalize_batched(_ptr(x), _ptr(y), bt, r, cc, int(steps), float(a), float(b), float(c),
+                                          float(eps), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
+    return y
+
+
+def mp_apply_update(w_hi: torch.Tensor, w_lo: torch.Tensor, v: torch.Tensor, eff_lr: float, decay: float,
+                    lr_mul_per_slot: torch.Tensor | None = None, stream=None) -> None:
+    """In place on (w_hi, w_lo): w = fp32(hi, lo); r = RN32(RN32(w*decay) - eta*v); split r.
+    The leading dimension is the slot (for the optional per-slot multiplier)."""
+    for t, n in ((w_hi, "w_hi"), (w_lo, "w_lo"), (v, "v")):
+        _dense(t, n, 2)
+    if w_lo.shape != w_hi.shape or v.shape != w_hi.shape:
+        raise ValueError("w_hi, w_lo and v must have one shape")
+    batch = w_hi.shape[0] if w_hi.dim() > 1 else 1
+    slot = w_hi.numel() // max(batch, 1)
+    if lr_mul_per_slot is not None:
+        _dense(lr_mul_per_slot, "lr_mul_per_slot", 4)
+    _check(lib().mp_apply_update(_ptr(w_hi), _ptr(w_lo), _ptr(v), batch, slot, float(eff_lr), float(decay),
+                                 _ptr(lr_mul_per_slot), _stream(stream)))
+
+
+def mb_timing_enable(on: bool) -> None:
+    lib().mb_timing_enable(1 if on else 0)
+
+
+def mb_timing_read() -> dict:
+    """{kernel name: (launches, total ms)} for the launches timed since the last read."""
+    buf = (mb_kernel_time * 64)()
+    n = lib().mb_timing_read(buf, 64)
+    if n < 0:
+        raise MuonBankError(8, "timing read failed")
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(min(n, 64))}

@@ -1,0 +1,80 @@
+// Shared device helpers for the gfx950 Muon bank kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mb {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define MB_LDS __attribute__((address_space(3)))
+
+// bf16 bits -> float (exact).
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// float -> bf16 bits, round to nearest even (finite inputs; inf stays inf).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t b = __float_as_uint(f);
+    b += 0x7FFFu + ((b >> 16) & 1u);
+    return (uint16_t)(b >> 16);
+}
+
+// Knuth's TwoSum: the exact error of s = RN(a + b), so that a + b = s + err.
+__device__ __forceinline__ double two_sum_err(double a, double b, double s) {
+    double bb = s - a;
+    return (a - (s - bb)) + (b - bb);
+}
+
+// Round-to-odd of the exact sum a + b to binary64: if the sum is not
+// representable, the neighbour with an odd last bit.  A later single
+// round-to-nearest to any format with at least two fewer significand bits
+// then equals the correctly rounded exact sum (Boldo and Melquiond, "Emulation
+// of FMA and correctly rounded sums: proved algorithms using rounding to odd").
+__device__ __forceinline__ double sum_round_odd(double a, double b) {
+    double s = a + b;
+    double e = two_sum_err(a, b, s);
+    if (e != 0.0) {
+        unsigned long long bits = (unsigned long long)__double_as_longlong(s);
+        if ((bits & 1ull) == 0ull) {
+            // the exact value lies between s and its neighbour in the direction of e
+            bits += ((e > 0.0) == (s > 0.0)) ? 1ull : ~0ull;
+            s = __longlong_as_double((long long)bits);
+        }
+    }
+    return s;
+}
+
+// Round a binary64 value that is already round-to-odd at 53 bits to float32,
+// round-to-nearest-even (53 >= 24 + 2, so this is the correct rounding of the
+// exact value).
+__device__ __forceinline__ float odd53_to_f32(double s) { return (float)s; }
+
+// Round a binary64 value that is round-to-odd at 53 bits to bf16 bits, round
+// to nearest even: first round-to-odd to float32 (24 >= 8 + 2), then RNE to bf16.
+__device__ __forceinline__ uint16_t odd53_to_bf16(double s) {
+    float f = (float)s;
+    if ((double)f != s) {
+        uint32_t b = __float_as_uint(f);
+        if ((b & 1u) == 0u) {
+            b += (fabs(s) > fabs((double)f)) ? 1u : 0xFFFFFFFFu;
+            f = __uint_as_float(b);
+        }
+    }
+    return f32_to_bf16_rne(f);
+}
+
+// Wavefront (64-lane) sum with a fixed reduction tree.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+}  // namespace mb

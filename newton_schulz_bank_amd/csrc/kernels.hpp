@@ -1,0 +1,48 @@
+// Host-side launchers of the gfx950 kernels (implemented in stream_kernels.hip
+// and ns_gemm.hip), used by the C ABI in muonbank.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mb {
+
+// Brackets kernel launches with events when kernel timing is on.
+struct RoundTimer {
+    virtual void begin(const char* name, hipStream_t stream) = 0;
+    virtual void end(hipStream_t stream) = 0;
+    virtual ~RoundTimer() = default;
+};
+
+// Elements per workgroup chunk of the streaming kernels and the chunk count per slot.
+int64_t stream_chunk_elems(bool vec);
+int stream_chunks(int64_t slot_numel, bool vec);
+
+// buf' and u (and, if partials is non-null, per-(slot, chunk) sums of u^2).
+hipError_t launch_momentum(const void* grad, void* buf, uint16_t* u, float* partials, int64_t batch,
+                           int64_t slot_numel, bool f32, bool vec, float mu, float nu, hipStream_t stream);
+// Per-(slot, chunk) sums of x^2 of a bf16 bank.
+hipError_t launch_sumsq(const uint16_t* x, float* partials, int64_t batch, int64_t slot_numel, bool vec,
+                        hipStream_t stream);
+// scale[i] = 1 / (sqrt(sum of slot i's partials) + eps); live[i] = (sum > 0).
+hipError_t launch_ns_scale(const float* partials, int nchunks, int64_t batch, float eps, float* scale, int* live,
+                           hipStream_t stream);
+// The mixed-precision apply on [batch, slot_numel].
+hipError_t launch_apply(uint16_t* w_hi, uint16_t* w_lo, const uint16_t* v, int64_t batch, int64_t slot_numel,
+                        bool vec, float eta, float decay, const float* lr_mul_per_slot, hipStream_t stream);
+
+// One Newton-Schulz round on a bank: x_out = round(x_in), with A and Bm as scratch.
+struct NsRound {
+    const uint16_t* x_in;
+    uint16_t* x_out;
+    uint16_t* A;
+    uint16_t* Bm;
+    int64_t batch, rows, cols;
+    float a, b, c;
+    bool first;            // apply the Frobenius scale (x_in is the unscaled input)
+    const float* scale;
+    const int* live;
+};
+hipError_t ns_round(const NsRound& r, hipStream_t stream, RoundTimer* timer);
+
+}  // namespace mb

@@ -1,0 +1,446 @@
+// C ABI of libmuonbank.so: argument validation, host scalars, workspace
+// layout and the launch sequence of the Muon bank step on one HIP stream.
+// The operations are stated in include/muonbank.h.
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kernels.hpp"
+#include "muonbank.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mb_status fail(mb_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+mb_status fail(mb_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+mb_status ok() {
+    g_last_error.clear();
+    return MB_OK;
+}
+
+// ---------------------------------------------------------------------------
+// kernel timing
+// ---------------------------------------------------------------------------
+
+struct TimedLaunch {
+    std::string name;
+    hipEvent_t start, stop;
+};
+
+std::mutex g_timing_mu;
+bool g_timing_on = false;
+std::vector<TimedLaunch> g_timed;
+
+struct Timer final : mb::RoundTimer {
+    TimedLaunch cur;
+    bool open = false;
+    void begin(const char* name, hipStream_t stream) override {
+        if (!g_timing_on) return;
+        cur.name = name;
+        if (hipEventCreate(&cur.start) != hipSuccess || hipEventCreate(&cur.stop) != hipSuccess) return;
+        (void)hipEventRecord(cur.start, stream);
+        open = true;
+    }
+    void end(hipStream_t stream) override {
+        if (!open) return;
+        (void)hipEventRecord(cur.stop, stream);
+        std::lock_guard<std::mutex> lk(g_timing_mu);
+        g_timed.push_back(cur);
+        open = false;
+    }
+};
+
+// ---------------------------------------------------------------------------
+// validation helpers
+// ---------------------------------------------------------------------------
+
+constexpr int64_t kMaxBatch = 65535;          // grid y dimension
+constexpr int64_t kMaxDim = (int64_t)1 << 30;   // rows, cols fit int with tile padding
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+mb_status check_shape(int64_t batch, int64_t rows, int64_t cols, const char* what) {
+    if (batch <= 0 || rows <= 0 || cols <= 0)
+        return fail(MB_ERR_SHAPE, "%s: batch, rows and cols must be positive (got %lld, %lld, %lld)", what,
+                    (long long)batch, (long long)rows, (long long)cols);
+    if (batch > kMaxBatch || rows > kMaxDim || cols > kMaxDim)
+        return fail(MB_ERR_SHAPE, "%s: shape (%lld, %lld, %lld) beyond the supported range (batch <= %lld, dims <= 2^30)",
+                    what, (long long)batch, (long long)rows, (long long)cols, (long long)kMaxBatch);
+    const int64_t slot = rows * cols;      // < 2^60
+    if (slot > ((int64_t)1 << 62) / batch)
+        return fail(MB_ERR_SHAPE, "%s: element count overflows", what);
+    return MB_OK;
+}
+
+struct Range {
+    uintptr_t lo, hi;
+    const char* name;
+};
+
+bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+mb_status check_no_overlap(const std::vector<Range>& rs) {
+    for (size_t i = 0; i < rs.size(); ++i)
+        for (size_t j = i + 1; j < rs.size(); ++j)
+            if (overlap(rs[i], rs[j]))
+                return fail(MB_ERR_ALIAS, "buffers %s and %s overlap", rs[i].name, rs[j].name);
+    return MB_OK;
+}
+
+bool is_finite(double v) { return std::isfinite(v); }
+
+mb_status check_hparams(const mb_hparams& hp) {
+    if (!is_finite(hp.lr) || !is_finite(hp.weight_decay) || !is_finite(hp.momentum) || !is_finite(hp.a) || !is_finite(hp.b) ||
+        !is_finite(hp.c) || !is_finite(hp.eps))
+        return fail(MB_ERR_VALUE, "hyper-parameters must be finite");
+    if (hp.ns_steps < 1 || hp.ns_steps > 64) return fail(MB_ERR_VALUE, "ns_steps must be in 1..64 (got %d)", hp.ns_steps);
+    if (hp.eps < 0) return fail(MB_ERR_VALUE, "eps must be >= 0");
+    return MB_OK;
+}
+
+size_t round_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Workspace of one bank: u, two ping-pong X buffers, A, B, partial sums, scale, live.
+struct BankWs {
+    size_t u, x1, x2, A, Bm, partials, scale, live, total;
+};
+
+BankWs bank_ws_layout(int64_t batch, int64_t rows, int64_t cols, bool vec) {
+    const int64_t m = rows < cols ? rows : cols;
+    BankWs w{};
+    size_t off = 0;
+    const size_t xb = round_up((size_t)(batch * rows * cols) * 2);
+    const size_t ab = round_up((size_t)(batch * m * m) * 2);
+    w.u = off; off += xb;
+    w.x1 = off; off += xb;
+    w.x2 = off; off += xb;
+    w.A = off; off += ab;
+    w.Bm = off; off += ab;
+    w.partials = off; off += round_up((size_t)batch * mb::stream_chunks(rows * cols, vec) * 4);
+    w.scale = off; off += round_up((size_t)batch * 4);
+    w.live = off; off += round_up((size_t)batch * 4);
+    w.total = off;
+    return w;
+}
+
+float f32(double v) { return (float)v; }
+
+// Newton-Schulz rounds on scaled input: x_first -> ... -> dest.  x1, x2 are
+// ping-pong buffers distinct from x_first and dest.
+mb_status run_ns(const uint16_t* x_first, uint16_t* dest, uint16_t* x1, uint16_t* x2, uint16_t* A, uint16_t* Bm,
+                 int64_t batch, int64_t rows, int64_t cols, int steps, double a, double b, double c,
+                 const float* scale, const int* live, hipStream_t stream, Timer& timer) {
+    const uint16_t* in = x_first;
+    for (int s = 0; s < steps; ++s) {
+        const bool last = s == steps - 1;
+        uint16_t* out = last ? dest : ((s & 1) ? x2 : x1);
+        mb::NsRound r{in, out, A, Bm, batch, rows, cols, f32(a), f32(b), f32(c), s == 0, scale, live};
+        hipError_t e = mb::ns_round(r, stream, &timer);
+        if (e != hipSuccess) return fail(MB_ERR_HIP, "Newton-Schulz round %d: %s", s, hipGetErrorString(e));
+        in = out;
+    }
+    return MB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void mb_default_hparams(mb_hparams* hp) {
+    if (!hp) return;
+    hp->lr = 0.02;
+    hp->weight_decay = 0.01;
+    hp->momentum = 0.95;
+    hp->ns_steps = 5;
+    hp->a = 3.4445;
+    hp->b = -4.7750;
+    hp->c = 2.0315;
+    hp->eps = 1e-7;
+}
+
+const char* mb_status_string(int32_t s) {
+    switch (s) {
+        case MB_OK: return "ok";
+        case MB_ERR_NULL: return "null pointer";
+        case MB_ERR_SHAPE: return "bad shape";
+        case MB_ERR_DTYPE: return "bad dtype";
+        case MB_ERR_ALIGN: return "misaligned pointer";
+        case MB_ERR_WORKSPACE: return "workspace too small";
+        case MB_ERR_ALIAS: return "overlapping buffers";
+        case MB_ERR_VALUE: return "bad scalar argument";
+        case MB_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+const char* mb_last_error(void) { return g_last_error.c_str(); }
+
+const char* mb_version(void) { return "muonbank 0.1 gfx950"; }
+
+size_t mb_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols) {
+    if (check_shape(batch, rows, cols, "mb_ns_workspace_bytes") != MB_OK) return 0;
+    const bool vec = (rows * cols) % 8 == 0;
+    return bank_ws_layout(batch, rows, cols, vec).total;
+}
+
+size_t mb_step_workspace_bytes(const mb_bank* banks, int32_t num_banks) {
+    if (!banks || num_banks <= 0) return 0;
+    size_t total = 0;
+    for (int32_t i = 0; i < num_banks; ++i) {
+        const mb_bank& b = banks[i];
+        if (check_shape(b.batch, b.rows, b.cols, "mb_step_workspace_bytes") != MB_OK) return 0;
+        total += bank_ws_layout(b.batch, b.rows, b.cols, (b.rows * b.cols) % 8 == 0).total;
+    }
+    return total;
+}
+
+mb_status muon_momentum_update(const void* grad, void* momentum, uint16_t* u_out, int64_t batch, int64_t rows,
+                               int64_t cols, int32_t dtype, float mu, float nu, void* stream) {
+    if (!grad || !momentum || !u_out) return fail(MB_ERR_NULL, "muon_momentum_update: null tensor pointer");
+    mb_status s = check_shape(batch, rows, cols, "muon_momentum_update");
+    if (s != MB_OK) return s;
+    if (dtype != MB_F32 && dtype != MB_BF16) return fail(MB_ERR_DTYPE, "muon_momentum_update: dtype %d", dtype);
+    if (!aligned16(grad) || !aligned16(momentum) || !aligned16(u_out))
+        return fail(MB_ERR_ALIGN, "muon_momentum_update: tensors must be 16-byte aligned");
+    if (!std::isfinite(mu) || !std::isfinite(nu)) return fail(MB_ERR_VALUE, "muon_momentum_update: mu, nu must be finite");
+    const int64_t n = batch * rows * cols;
+    const size_t es = dtype == MB_F32 ? 4 : 2;
+    s = check_no_overlap({{(uintptr_t)grad, (uintptr_t)grad + n * es, "grad"},
+                          {(uintptr_t)momentum, (uintptr_t)momentum + n * es, "momentum"},
+                          {(uintptr_t)u_out, (uintptr_t)u_out + n * 2, "u_out"}});
+    if (s != MB_OK) return s;
+    const bool vec = (rows * cols) % 8 == 0;
+    Timer timer;
+    timer.begin("momentum", (hipStream_t)stream);
+    hipError_t e = mb::launch_momentum(grad, momentum, u_out, nullptr, batch, rows * cols, dtype == MB_F32, vec, mu, nu,
+                                       (hipStream_t)stream);
+    timer.end((hipStream_t)stream);
+    if (e != hipSuccess) return fail(MB_ERR_HIP, "momentum launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+mb_status ns_orthogonalize_batched(const uint16_t* x, uint16_t* y, int64_t batch, int64_t rows, int64_t cols,
+                                   int32_t steps, double a, double b, double c, double eps, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    if (!x || !y) return fail(MB_ERR_NULL, "ns_orthogonalize_batched: null tensor pointer");
+    mb_status s = check_shape(batch, rows, cols, "ns_orthogonalize_batched");
+    if (s != MB_OK) return s;
+    if (!aligned16(x) || !aligned16(y) || (workspace && !aligned16(workspace)))
+        return fail(MB_ERR_ALIGN, "ns_orthogonalize_batched: pointers must be 16-byte aligned");
+    if (steps < 1 || steps > 64) return fail(MB_ERR_VALUE, "ns_orthogonalize_batched: steps must be in 1..64");
+    if (!is_finite(a) || !is_finite(b) || !is_finite(c) || !is_finite(eps) || eps < 0)
+        return fail(MB_ERR_VALUE, "ns_orthogonalize_batched: coefficients must be finite and eps >= 0");
+    const bool vec = (rows * cols) % 8 == 0;
+    const BankWs L = bank_ws_layout(batch, rows, cols, vec);
+    if (!workspace || workspace_bytes < L.total)
+        return fail(MB_ERR_WORKSPACE, "ns_orthogonalize_batched: workspace of %zu bytes needed, %zu given", L.total,
+                    workspace ? workspace_bytes : (size_t)0);
+    const int64_t n = batch * rows * cols;
+    const Range rx{(uintptr_t)x, (uintptr_t)x + n * 2, "x"};
+    const Range ry{(uintptr_t)y, (uintptr_t)y + n * 2, "y"};
+    const Range rw{(uintptr_t)workspace, (uintptr_t)workspace + L.total, "workspace"};
+    if (x != y) {
+        s = check_no_overlap({rx, ry, rw});
+    } else {
+        s = check_no_overlap({rx, rw});
+    }
+    if (s != MB_OK) return s;
+
+    hipStream_t st = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    float* partials = (float*)(ws + L.partials);
+    float* scale = (float*)(ws + L.scale);
+    int* live = (int*)(ws + L.live);
+    uint16_t* x1 = (uint16_t*)(ws + L.x1);
+    uint16_t* x2 = (uint16_t*)(ws + L.x2);
+    Timer timer;
+    timer.begin("sumsq", st);
+    hipError_t e = mb::launch_sumsq(x, partials, batch, rows * cols, vec, st);
+    timer.end(st);
+    if (e != hipSuccess) return fail(MB_ERR_HIP, "sumsq launch: %s", hipGetErrorString(e));
+    timer.begin("ns_scale", st);
+    e = mb::launch_ns_scale(partials, mb::stream_chunks(rows * cols, vec), batch, f32(eps), scale, live, st);
+    timer.end(st);
+    if (e != hipSuccess) return fail(MB_ERR_HIP, "ns_scale launch: %s", hipGetErrorString(e));
+    // in place with a single round: write the round to scratch, then copy
+    uint16_t* dest = (x == y && steps == 1) ? (uint16_t*)(ws + L.u) : y;
+    s = run_ns(x, dest, x1, x2, (uint16_t*)(ws + L.A), (uint16_t*)(ws + L.Bm), batch, rows, cols, steps, a, b, c,
+               scale, live, st, timer);
+    if (s != MB_OK) return s;
+    if (dest != y) {
+        e = hipMemcpyAsync(y, dest, n * 2, hipMemcpyDeviceToDevice, st);
+        if (e != hipSuccess) return fail(MB_ERR_HIP, "copy: %s", hipGetErrorString(e));
+    }
+    return ok();
+}
+
+mb_status mp_apply_update(uint16_t* w_hi, uint16_t* w_lo, const uint16_t* v, int64_t batch, int64_t slot_numel,
+                          float eff_lr, float decay, const float* lr_mul_per_slot, void* stream) {
+    if (!w_hi || !w_lo || !v) return fail(MB_ERR_NULL, "mp_apply_update: null tensor pointer");
+    mb_status s = check_shape(batch, 1, slot_numel, "mp_apply_update");
+    if (s != MB_OK) return s;
+    if (!aligned16(w_hi) || !aligned16(w_lo) || !aligned16(v) || ((uintptr_t)lr_mul_per_slot & 3u))
+        return fail(MB_ERR_ALIGN, "mp_apply_update: tensors must be 16-byte aligned (lr_mul_per_slot 4-byte)");
+    if (!std::isfinite(eff_lr) || !std::isfinite(decay))
+        return fail(MB_ERR_VALUE, "mp_apply_update: eff_lr and decay must be finite");
+    const int64_t n = batch * slot_numel;
+    std::vector<Range> rs = {{(uintptr_t)w_hi, (uintptr_t)w_hi + n * 2, "w_hi"},
+                             {(uintptr_t)w_lo, (uintptr_t)w_lo + n * 2, "w_lo"},
+                             {(uintptr_t)v, (uintptr_t)v + n * 2, "v"}};
+    if (lr_mul_per_slot) rs.push_back({(uintptr_t)lr_mul_per_slot, (uintptr_t)lr_mul_per_slot + batch * 4, "lr_mul_per_slot"});
+    s = check_no_overlap(rs);
+    if (s != MB_OK) return s;
+    Timer timer;
+    timer.begin("apply", (hipStream_t)stream);
+    hipError_t e = mb::launch_apply(w_hi, w_lo, v, batch, slot_numel, slot_numel % 8 == 0, eff_lr, decay,
+                                    lr_mul_per_slot, (hipStream_t)stream);
+    timer.end((hipStream_t)stream);
+    if (e != hipSuccess) return fail(MB_ERR_HIP, "apply launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+mb_status muon_bank_step(const mb_bank* banks, int32_t num_banks, const mb_hparams* hp_in, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    if (!banks) return fail(MB_ERR_NULL, "muon_bank_step: banks is null");
+    if (num_banks <= 0 || num_banks > 1024) return fail(MB_ERR_SHAPE, "muon_bank_step: num_banks must be in 1..1024");
+    mb_hparams hp;
+    if (hp_in) hp = *hp_in;
+    else mb_default_hparams(&hp);
+    mb_status s = check_hparams(hp);
+    if (s != MB_OK) return s;
+
+    // ---- validate every bank before enqueueing anything
+    std::vector<Range> ranges;
+    size_t need = 0;
+    for (int32_t i = 0; i < num_banks; ++i) {
+        const mb_bank& b = banks[i];
+        if (!b.grad || !b.momentum || !b.w_hi || !b.w_lo)
+            return fail(MB_ERR_NULL, "muon_bank_step: bank %d has a null tensor pointer", i);
+        s = check_shape(b.batch, b.rows, b.cols, "muon_bank_step");
+        if (s != MB_OK) return s;
+        if (b.grad_dtype != MB_F32 && b.grad_dtype != MB_BF16)
+            return fail(MB_ERR_DTYPE, "muon_bank_step: bank %d dtype %d", i, b.grad_dtype);
+        if (!aligned16(b.grad) || !aligned16(b.momentum) || !aligned16(b.w_hi) || !aligned16(b.w_lo) ||
+            !aligned16(b.v_out) || !aligned16(b.u_out) || ((uintptr_t)b.lr_mul_per_slot & 3u))
+            return fail(MB_ERR_ALIGN, "muon_bank_step: bank %d tensors must be 16-byte aligned", i);
+        if (!is_finite(b.lr_mul) || !is_finite(b.wd_mul)) return fail(MB_ERR_VALUE, "muon_bank_step: bank %d multipliers", i);
+        const int64_t n = b.batch * b.rows * b.cols;
+        const size_t es = b.grad_dtype == MB_F32 ? 4 : 2;
+        ranges.push_back({(uintptr_t)b.grad, (uintptr_t)b.grad + n * es, "grad"});
+        ranges.push_back({(uintptr_t)b.momentum, (uintptr_t)b.momentum + n * es, "momentum"});
+        ranges.push_back({(uintptr_t)b.w_hi, (uintptr_t)b.w_hi + n * 2, "w_hi"});
+        ranges.push_back({(uintptr_t)b.w_lo, (uintptr_t)b.w_lo + n * 2, "w_lo"});
+        if (b.v_out) ranges.push_back({(uintptr_t)b.v_out, (uintptr_t)b.v_out + n * 2, "v_out"});
+        if (b.u_out) ranges.push_back({(uintptr_t)b.u_out, (uintptr_t)b.u_out + n * 2, "u_out"});
+        if (b.lr_mul_per_slot)
+            ranges.push_back({(uintptr_t)b.lr_mul_per_slot, (uintptr_t)b.lr_mul_per_slot + b.batch * 4, "lr_mul_per_slot"});
+        need += bank_ws_layout(b.batch, b.rows, b.cols, (b.rows * b.cols) % 8 == 0).total;
+    }
+    if (!workspace || workspace_bytes < need)
+        return fail(MB_ERR_WORKSPACE, "muon_bank_step: workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(MB_ERR_ALIGN, "muon_bank_step: workspace must be 16-byte aligned");
+    ranges.push_back({(uintptr_t)workspace, (uintptr_t)workspace + need, "workspace"});
+    s = check_no_overlap(ranges);
+    if (s != MB_OK) return s;
+
+    // ---- enqueue
+    hipStream_t st = (hipStream_t)stream;
+    Timer timer;
+    char* ws = (char*)workspace;
+    for (int32_t i = 0; i < num_banks; ++i) {
+        const mb_bank& b = banks[i];
+        const int64_t slot = b.rows * b.cols;
+        const bool vec = slot % 8 == 0;
+        const BankWs L = bank_ws_layout(b.batch, b.rows, b.cols, vec);
+        // host scalars in double, rounded once to float32
+        const float mu = f32(hp.momentum);
+        const float nu = f32(1.0 - hp.momentum);
+        const float decay = f32(1.0 - hp.lr * hp.weight_decay * b.wd_mul);
+        const float eta = f32(hp.lr * std::sqrt(std::max(1.0, (double)b.rows / (double)b.cols)) * b.lr_mul);
+
+        uint16_t* u = b.u_out ? b.u_out : (uint16_t*)(ws + L.u);
+        uint16_t* v = b.v_out ? b.v_out : (uint16_t*)(ws + L.u);   // u is dead once the first round has read it
+        float* partials = (float*)(ws + L.partials);
+        float* scale = (float*)(ws + L.scale);
+        int* live = (int*)(ws + L.live);
+
+        timer.begin("momentum", st);
+        hipError_t e = mb::launch_momentum(b.grad, b.momentum, u, partials, b.batch, slot, b.grad_dtype == MB_F32, vec,
+                                           mu, nu, st);
+        timer.end(st);
+        if (e != hipSuccess) return fail(MB_ERR_HIP, "momentum launch: %s", hipGetErrorString(e));
+        timer.begin("ns_scale", st);
+        e = mb::launch_ns_scale(partials, mb::stream_chunks(slot, vec), b.batch, f32(hp.eps), scale, live, st);
+        timer.end(st);
+        if (e != hipSuccess) return fail(MB_ERR_HIP, "ns_scale launch: %s", hipGetErrorString(e));
+        // with one round and no v_out, the round would read u while writing v in the same buffer
+        uint16_t* dest = (hp.ns_steps == 1 && v == u) ? (uint16_t*)(ws + L.x2) : v;
+        s = run_ns(u, dest, (uint16_t*)(ws + L.x1), (uint16_t*)(ws + L.x2), (uint16_t*)(ws + L.A),
+                   (uint16_t*)(ws + L.Bm), b.batch, b.rows, b.cols, hp.ns_steps, hp.a, hp.b, hp.c, scale, live, st,
+                   timer);
+        if (s != MB_OK) return s;
+        timer.begin("apply", st);
+        e = mb::launch_apply(b.w_hi, b.w_lo, dest, b.batch, slot, vec, eta, decay, b.lr_mul_per_slot, st);
+        timer.end(st);
+        if (e != hipSuccess) return fail(MB_ERR_HIP, "apply launch: %s", hipGetErrorString(e));
+        if (dest != v) {
+            e = hipMemcpyAsync(v, dest, (size_t)(b.batch * slot) * 2, hipMemcpyDeviceToDevice, st);
+            if (e != hipSuccess) return fail(MB_ERR_HIP, "copy: %s", hipGetErrorString(e));
+        }
+    }
+    return ok();
+}
+
+void mb_timing_enable(int32_t on) {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    g_timing_on = on != 0;
+}
+
+int32_t mb_timing_read(mb_kernel_time* out, int32_t max_entries) {
+    std::vector<TimedLaunch> launches;
+    {
+        std::lock_guard<std::mutex> lk(g_timing_mu);
+        launches.swap(g_timed);
+    }
+    std::vector<mb_kernel_time> agg;
+    int32_t rc = 0;
+    for (auto& t : launches) {
+        float ms = 0.f;
+        if (hipEventSynchronize(t.stop) != hipSuccess || hipEventElapsedTime(&ms, t.start, t.stop) != hipSuccess) rc = -1;
+        (void)hipEventDestroy(t.start);
+        (void)hipEventDestroy(t.stop);
+        size_t k = 0;
+        for (; k < agg.size(); ++k)
+            if (t.name == agg[k].name) break;
+        if (k == agg.size()) {
+            mb_kernel_time z{};
+            std::snprintf(z.name, sizeof z.name, "%s", t.name.c_str());
+            agg.push_back(z);
+        }
+        agg[k].launches += 1;
+        agg[k].total_ms += ms;
+    }
+    if (rc < 0) return -1;
+    const int32_t n = (int32_t)agg.size();
+    for (int32_t i = 0; i < n && i < max_entries && out; ++i) out[i] = agg[i];
+    return n;
+}
+
+}  // extern "C"

@@ -1,0 +1,287 @@
+// Bandwidth-bound kernels of the Muon bank step on gfx950:
+//   * momentum + Nesterov update, with per-slot partial sums of u^2 for the
+//     Frobenius pre-scale;
+//   * partial sums of x^2 for a stand-alone Newton-Schulz call;
+//   * the per-slot scale s = 1 / (||u||_F + eps) and live flag;
+//   * the mixed-precision apply on bf16 weight + uint16 low mantissa.
+//
+// Momentum follows the two lerps of "Muon Custom Sizing", section 4
+// (buf' = mu*buf + (1-mu)*g, then u = (1-mu)*g + mu*buf'); the apply follows
+// the Record 7 walkthrough, section 4.1 (recombine, decay, add, split).
+//
+// Compiled with -ffp-contract=off: every rounding below is the one written.
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace mb {
+
+// ---------------------------------------------------------------------------
+// momentum + Nesterov
+// ---------------------------------------------------------------------------
+
+// Exact products in binary64 (<=24-bit x <=24-bit significands), a
+// round-to-odd sum, then one rounding to the storage format: buf' and u are
+// the correctly rounded exact values.
+__device__ __forceinline__ void momentum_elem(float g, float b, float mu, float nu, float& buf_new_f32,
+                                              uint16_t& buf_new_bf16, uint16_t& u_bits, bool f32_storage,
+                                              float& u_val) {
+    double p_buf = (double)mu * (double)b;
+    double p_g = (double)nu * (double)g;
+    double s = sum_round_odd(p_buf, p_g);
+    float stored;
+    if (f32_storage) {
+        buf_new_f32 = odd53_to_f32(s);
+        stored = buf_new_f32;
+    } else {
+        buf_new_bf16 = odd53_to_bf16(s);
+        stored = bf16_to_f32(buf_new_bf16);
+    }
+    double s2 = sum_round_odd(p_g, (double)mu * (double)stored);
+    u_bits = odd53_to_bf16(s2);
+    u_val = bf16_to_f32(u_bits);
+}
+
+template <bool F32, bool VEC>
+__global__ void __launch_bounds__(256) momentum_kernel(const void* __restrict__ grad_, void* __restrict__ buf_,
+                                                       uint16_t* __restrict__ u, float* __restrict__ partials,
+                                                       int64_t slot_numel, int64_t chunk_elems, float mu, float nu) {
+    const int64_t slot = blockIdx.y;
+    const int64_t chunk = blockIdx.x;
+    const int64_t base = slot * slot_numel;
+    const int64_t lo = chunk * chunk_elems;
+    const int64_t hi = min(lo + chunk_elems, slot_numel);
+    float acc = 0.f;
+    if (VEC) {
+        // 8 consecutive elements per thread per step; slot_numel % 8 == 0 and bases are 16-byte aligned
+        for (int64_t e = lo + (int64_t)threadIdx.x * 8; e < hi; e += 256 * 8) {
+            const int64_t idx = base + e;
+            float g[8], b[8];
+            if (F32) {
+                const float4* gp = reinterpret_cast<const float4*>((const float*)grad_ + idx);
+                const float4* bp = reinterpret_cast<const float4*>((const float*)buf_ + idx);
+                float4 g0 = gp[0], g1 = gp[1], b0 = bp[0], b1 = bp[1];
+                g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w; g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
+                b[0] = b0.x; b[1] = b0.y; b[2] = b0.z; b[3] = b0.w; b[4] = b1.x; b[5] = b1.y; b[6] = b1.z; b[7] = b1.w;
+            } else {
+                u32x4 gv = *reinterpret_cast<const u32x4*>((const uint16_t*)grad_ + idx);
+                u32x4 bv = *reinterpret_cast<const u32x4*>((const uint16_t*)buf_ + idx);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    g[2 * q] = __uint_as_float(gv[q] << 16);
+                    g[2 * q + 1] = __uint_as_float(gv[q] & 0xFFFF0000u);
+                    b[2 * q] = __uint_as_float(bv[q] << 16);
+                    b[2 * q + 1] = __uint_as_float(bv[q] & 0xFFFF0000u);
+                }
+            }
+            float bn32[8];
+            uint16_t bn16[8], ub[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                float uv;
+                momentum_elem(g[q], b[q], mu, nu, bn32[q], bn16[q], ub[q], F32, uv);
+                acc = __fmaf_rn(uv, uv, acc);
+            }
+            if (F32) {
+                float4* bp = reinterpret_cast<float4*>((float*)buf_ + idx);
+                bp[0] = make_float4(bn32[0], bn32[1], bn32[2], bn32[3]);
+                bp[1] = make_float4(bn32[4], bn32[5], bn32[6], bn32[7]);
+            } else {
+                u32x4 bo;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) bo[q] = (uint32_t)bn16[2 * q] | ((uint32_t)bn16[2 * q + 1] << 16);
+                *reinterpret_cast<u32x4*>((uint16_t*)buf_ + idx) = bo;
+            }
+            u32x4 uo;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) uo[q] = (uint32_t)ub[2 * q] | ((uint32_t)ub[2 * q + 1] << 16);
+            *reinterpret_cast<u32x4*>(u + idx) = uo;
+        }
+    } else {
+        for (int64_t e = lo + threadIdx.x; e < hi; e += 256) {
+            const int64_t idx = base + e;
+            float g, b;
+            if (F32) {
+                g = ((const float*)grad_)[idx];
+                b = ((const float*)buf_)[idx];
+            } else {
+                g = bf16_to_f32(((const uint16_t*)grad_)[idx]);
+                b = bf16_to_f32(((const uint16_t*)buf_)[idx]);
+            }
+            float bn32, uv;
+            uint16_t bn16, ub;
+            momentum_elem(g, b, mu, nu, bn32, bn16, ub, F32, uv);
+            acc = __fmaf_rn(uv, uv, acc);
+            if (F32) ((float*)buf_)[idx] = bn32;
+            else ((uint16_t*)buf_)[idx] = bn16;
+            u[idx] = ub;
+        }
+    }
+    // block reduction in a fixed order: wave tree, then wave 0 adds the four wave sums
+    __shared__ float red[4];
+    acc = wave_sum(acc);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0 && partials) partials[slot * gridDim.x + chunk] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// ---------------------------------------------------------------------------
+// sum of squares of a bf16 bank (Frobenius norm of the input of a stand-alone NS)
+// ---------------------------------------------------------------------------
+
+template <bool VEC>
+__global__ void __launch_bounds__(256) sumsq_kernel(const uint16_t* __restrict__ x, float* __restrict__ partials,
+                                                    int64_t slot_numel, int64_t chunk_elems) {
+    const int64_t slot = blockIdx.y;
+    const int64_t chunk = blockIdx.x;
+    const int64_t base = slot * slot_numel;
+    const int64_t lo = chunk * chunk_elems;
+    const int64_t hi = min(lo + chunk_elems, slot_numel);
+    float acc = 0.f;
+    if (VEC) {
+        for (int64_t e = lo + (int64_t)threadIdx.x * 8; e < hi; e += 256 * 8) {
+            u32x4 v = *reinterpret_cast<const u32x4*>(x + base + e);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float a = __uint_as_float(v[q] << 16), b = __uint_as_float(v[q] & 0xFFFF0000u);
+                acc = __fmaf_rn(a, a, acc);
+                acc = __fmaf_rn(b, b, acc);
+            }
+        }
+    } else {
+        for (int64_t e = lo + threadIdx.x; e < hi; e += 256) {
+            float a = bf16_to_f32(x[base + e]);
+            acc = __fmaf_rn(a, a, acc);
+        }
+    }
+    __shared__ float red[4];
+    acc = wave_sum(acc);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) partials[slot * gridDim.x + chunk] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// ---------------------------------------------------------------------------
+// per-slot scale and live flag: one wavefront per slot, fixed order
+// ---------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(64) ns_scale_kernel(const float* __restrict__ partials, int nchunks, float eps,
+                                                      float* __restrict__ scale, int* __restrict__ live) {
+    const int slot = blockIdx.x;
+    float acc = 0.f;
+    for (int i = threadIdx.x; i < nchunks; i += 64) acc += partials[(int64_t)slot * nchunks + i];
+    acc = wave_sum(acc);
+    if (threadIdx.x == 0) {
+        float nrm = sqrtf(acc);
+        scale[slot] = 1.0f / (nrm + eps);
+        live[slot] = acc > 0.f ? 1 : 0;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// mixed-precision apply
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t apply_elem(uint32_t hi, uint32_t lo, uint32_t v, float eta, float decay) {
+    float w = __uint_as_float((hi << 16) | lo);
+    float t = __fmul_rn(w, decay);
+    float r = __fmaf_rn(-eta, __uint_as_float(v << 16), t);
+    return __float_as_uint(r);
+}
+
+// VEC: 8 elements per thread per step (slot_numel % 8 == 0, 16-byte aligned bases).
+template <bool VEC, bool PER_SLOT>
+__global__ void __launch_bounds__(256) apply_kernel(uint16_t* __restrict__ w_hi, uint16_t* __restrict__ w_lo,
+                                                    const uint16_t* __restrict__ v, int64_t slot_numel,
+                                                    int64_t chunk_elems, float eta, float decay,
+                                                    const float* __restrict__ lr_mul_per_slot) {
+    const int64_t slot = blockIdx.y;
+    const int64_t base = slot * slot_numel;
+    const int64_t lo = (int64_t)blockIdx.x * chunk_elems;
+    const int64_t hi = min(lo + chunk_elems, slot_numel);
+    const float eta_s = PER_SLOT ? __fmul_rn(eta, lr_mul_per_slot[slot]) : eta;
+    if (VEC) {
+        for (int64_t e = lo + (int64_t)threadIdx.x * 8; e < hi; e += 256 * 8) {
+            const int64_t idx = base + e;
+            u32x4 h = *reinterpret_cast<const u32x4*>(w_hi + idx);
+            u32x4 l = *reinterpret_cast<const u32x4*>(w_lo + idx);
+            u32x4 vv = *reinterpret_cast<const u32x4*>(v + idx);
+            u32x4 ho, lo2;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t r0 = apply_elem(h[q] & 0xFFFFu, l[q] & 0xFFFFu, vv[q] & 0xFFFFu, eta_s, decay);
+                uint32_t r1 = apply_elem(h[q] >> 16, l[q] >> 16, vv[q] >> 16, eta_s, decay);
+                ho[q] = (r0 >> 16) | (r1 & 0xFFFF0000u);
+                lo2[q] = (r0 & 0xFFFFu) | (r1 << 16);
+            }
+            *reinterpret_cast<u32x4*>(w_hi + idx) = ho;
+            *reinterpret_cast<u32x4*>(w_lo + idx) = lo2;
+        }
+    } else {
+        for (int64_t e = lo + threadIdx.x; e < hi; e += 256) {
+            const int64_t idx = base + e;
+            uint32_t r = apply_elem(w_hi[idx], w_lo[idx], v[idx], eta_s, decay);
+            w_hi[idx] = (uint16_t)(r >> 16);
+            w_lo[idx] = (uint16_t)(r & 0xFFFFu);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host-side launchers
+// ---------------------------------------------------------------------------
+
+int64_t stream_chunk_elems(bool vec) { return vec ? 16384 : 4096; }
+
+int stream_chunks(int64_t slot_numel, bool vec) {
+    // fixed chunks of stream_chunk_elems() elements (a multiple of 8), so every
+    // thread's 8-element group stays inside one slot and one chunk
+    const int64_t per = stream_chunk_elems(vec);
+    int64_t n = (slot_numel + per - 1) / per;
+    return (int)(n < 1 ? 1 : n);
+}
+
+hipError_t launch_momentum(const void* grad, void* buf, uint16_t* u, float* partials, int64_t batch,
+                           int64_t slot_numel, bool f32, bool vec, float mu, float nu, hipStream_t stream) {
+    const int64_t chunk = stream_chunk_elems(vec);
+    dim3 grid((unsigned)stream_chunks(slot_numel, vec), (unsigned)batch);
+    if (f32) {
+        if (vec) momentum_kernel<true, true><<<grid, 256, 0, stream>>>(grad, buf, u, partials, slot_numel, chunk, mu, nu);
+        else momentum_kernel<true, false><<<grid, 256, 0, stream>>>(grad, buf, u, partials, slot_numel, chunk, mu, nu);
+    } else {
+        if (vec) momentum_kernel<false, true><<<grid, 256, 0, stream>>>(grad, buf, u, partials, slot_numel, chunk, mu, nu);
+        else momentum_kernel<false, false><<<grid, 256, 0, stream>>>(grad, buf, u, partials, slot_numel, chunk, mu, nu);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_sumsq(const uint16_t* x, float* partials, int64_t batch, int64_t slot_numel, bool vec,
+                        hipStream_t stream) {
+    const int64_t chunk = stream_chunk_elems(vec);
+    dim3 grid((unsigned)stream_chunks(slot_numel, vec), (unsigned)batch);
+    if (vec) sumsq_kernel<true><<<grid, 256, 0, stream>>>(x, partials, slot_numel, chunk);
+    else sumsq_kernel<false><<<grid, 256, 0, stream>>>(x, partials, slot_numel, chunk);
+    return hipGetLastError();
+}
+
+hipError_t launch_ns_scale(const float* partials, int nchunks, int64_t batch, float eps, float* scale, int* live,
+                           hipStream_t stream) {
+    ns_scale_kernel<<<(unsigned)batch, 64, 0, stream>>>(partials, nchunks, eps, scale, live);
+    return hipGetLastError();
+}
+
+hipError_t launch_apply(uint16_t* w_hi, uint16_t* w_lo, const uint16_t* v, int64_t batch, int64_t slot_numel,
+                        bool vec, float eta, float decay, const float* lr_mul_per_slot, hipStream_t stream) {
+    const int64_t chunk = stream_chunk_elems(vec);
+    dim3 grid((unsigned)stream_chunks(slot_numel, vec), (unsigned)batch);
+    if (lr_mul_per_slot) {
+        if (vec) apply_kernel<true, true><<<grid, 256, 0, stream>>>(w_hi, w_lo, v, slot_numel, chunk, eta, decay, lr_mul_per_slot);
+        else apply_kernel<false, true><<<grid, 256, 0, stream>>>(w_hi, w_lo, v, slot_numel, chunk, eta, decay, lr_mul_per_slot);
+    } else {
+        if (vec) apply_kernel<true, false><<<grid, 256, 0, stream>>>(w_hi, w_lo, v, slot_numel, chunk, eta, decay, nullptr);
+        else apply_kernel<false, false><<<grid, 256, 0, stream>>>(w_hi, w_lo, v, slot_numel, chunk, eta, decay, nullptr);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace mb

@@ -1,0 +1,148 @@
+"""The C ABI without a GPU: symbols, defaults, workspace queries and every
+validation error path (all of which return before anything is launched)."""
+
+import ctypes
+import json
+import math
+import os
+import re
+
+import pytest
+
+from newton_schulz_bank_amd import api
+from tests.conftest import GOLDEN, ROOT
+
+HEADER = os.path.join(ROOT, "include", "muonbank.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, ALIAS, VALUE = 0, 1, 2, 3, 4, 5, 6, 7
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)) - {"if"})
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(api.LIB_PATH):
+        from newton_schulz_bank_amd import build
+        build.build()
+    return api.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = header_functions()
+    assert set(names) == set(api.EXPORTED), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_default_hparams_are_the_pages_values(L):
+    coef = json.load(open(os.path.join(GOLDEN, "ns_coefficients.json")))
+    dflt = json.load(open(os.path.join(GOLDEN, "muon_defaults.json")))
+    hp = api.default_hparams()
+    assert (hp.a, hp.b, hp.c, hp.ns_steps) == (coef["a"], coef["b"], coef["c"], coef["steps"])
+    assert (hp.lr, hp.weight_decay, hp.momentum) == (dflt["lr"], dflt["weight_decay"], dflt["momentum"])
+    assert hp.eps == 1e-7
+    assert L.mb_version().decode().startswith("muonbank")
+
+
+def test_status_strings(L):
+    assert L.mb_status_string(0) == b"ok"
+    assert L.mb_status_string(5) == b"workspace too small"
+    assert L.mb_status_string(99) == b"unknown status"
+
+
+def test_workspace_queries(L):
+    w1 = L.mb_ns_workspace_bytes(40, 768, 768)
+    assert w1 >= 3 * 40 * 768 * 768 * 2 + 2 * 40 * 768 * 768 * 2
+    assert L.mb_ns_workspace_bytes(24, 3072, 768) > w1
+    assert L.mb_ns_workspace_bytes(0, 768, 768) == 0
+    assert L.mb_ns_workspace_bytes(1, -1, 768) == 0
+    b = api.mb_bank(40, 768, 768, api.MB_BF16, 1.0, 1.0, 0x10000, 0x20000, 0x30000, 0x40000, None, None, None)
+    arr = (api.mb_bank * 2)(b, b)
+    assert L.mb_step_workspace_bytes(arr, 2) == 2 * L.mb_step_workspace_bytes(arr, 1) == 2 * w1
+    assert L.mb_step_workspace_bytes(arr, 0) == 0
+
+
+def _bank(batch=4, rows=64, cols=64, dtype=api.MB_BF16, base=1 << 32, **over):
+    n = batch * rows * cols
+    es = 4 if dtype == api.MB_F32 else 2
+    span = (n * max(es, 2) + 4095) // 4096 * 4096
+    fields = dict(batch=batch, rows=rows, cols=cols, grad_dtype=dtype, lr_mul=1.0, wd_mul=1.0,
+                  grad=base, momentum=base + span, w_hi=base + 2 * span, w_lo=base + 3 * span,
+                  lr_mul_per_slot=None, v_out=None, u_out=None)
+    fields.update(over)
+    b = api.mb_bank()
+    for k, v in fields.items():
+        setattr(b, k, v)
+    return b, base + 8 * span
+
+
+def _step(L, banks, ws, ws_bytes, hp=None):
+    arr = (api.mb_bank * len(banks))(*banks)
+    return L.muon_bank_step(arr, len(banks), ctypes.byref(hp) if hp is not None else None, ws, ws_bytes, None)
+
+
+def test_step_validation_errors(L):
+    good, ws = _bank()
+    need = L.mb_step_workspace_bytes((api.mb_bank * 1)(good), 1)
+    assert _step(L, [_bank(grad=None)[0]], ws, need) == NULL
+    assert L.muon_bank_step(None, 1, None, ws, need, None) == NULL
+    assert _step(L, [_bank(rows=0)[0]], ws, need) == SHAPE
+    assert _step(L, [_bank(batch=70000)[0]], ws, need) == SHAPE
+    assert _step(L, [_bank(dtype=7)[0]], ws, need) == DTYPE
+    assert _step(L, [_bank(grad=(1 << 32) + 2)[0]], ws, need) == ALIGN
+    assert _step(L, [_bank(v_out=(1 << 40) + 8)[0]], ws, need) == ALIGN
+    assert _step(L, [_bank(lr_mul_per_slot=(1 << 40) + 2)[0]], ws, need) == ALIGN
+    assert _step(L, [good], ws, need - 1) == WORKSPACE
+    assert _step(L, [good], None, need) == WORKSPACE
+    # buffers overlapping each other, the workspace, or another bank
+    assert _step(L, [_bank(momentum=good.grad + 1024)[0]], ws, need) == ALIAS
+    assert _step(L, [good], good.w_lo, need) == ALIAS
+    two = (api.mb_bank * 2)(good, good)
+    assert L.muon_bank_step(two, 2, None, ws, 2 * need, None) == ALIAS
+    hp = api.default_hparams()
+    hp.ns_steps = 0
+    assert _step(L, [good], ws, need, hp) == VALUE
+    hp = api.default_hparams()
+    hp.lr = math.nan
+    assert _step(L, [good], ws, need, hp) == VALUE
+    assert _step(L, [_bank(lr_mul=math.inf)[0]], ws, need) == VALUE
+    assert len(L.mb_last_error()) > 0
+
+
+def test_stage_entry_point_validation_errors(L):
+    p = 1 << 36
+    # momentum
+    assert L.muon_momentum_update(None, p, p + (1 << 30), 1, 8, 8, 1, 0.95, 0.05, None) == NULL
+    assert L.muon_momentum_update(p, p + (1 << 30), p + (2 << 30), 1, 8, 8, 9, 0.95, 0.05, None) == DTYPE
+    assert L.muon_momentum_update(p, p + (1 << 30), p + (2 << 30), 0, 8, 8, 1, 0.95, 0.05, None) == SHAPE
+    assert L.muon_momentum_update(p + 4, p + (1 << 30), p + (2 << 30), 1, 8, 8, 1, 0.95, 0.05, None) == ALIGN
+    assert L.muon_momentum_update(p, p + 64, p + (2 << 30), 1, 8, 8, 1, 0.95, 0.05, None) == ALIAS
+    assert L.muon_momentum_update(p, p + (1 << 30), p + (2 << 30), 1, 8, 8, 1, math.nan, 0.05, None) == VALUE
+    # Newton-Schulz
+    need = L.mb_ns_workspace_bytes(2, 64, 64)
+    ws = p + (4 << 30)
+    assert L.ns_orthogonalize_batched(None, p, 2, 64, 64, 5, 3.4445, -4.775, 2.0315, 1e-7, ws, need, None) == NULL
+    assert L.ns_orthogonalize_batched(p, p + (1 << 30), 2, 64, 0, 5, 3.4445, -4.775, 2.0315, 1e-7, ws, need, None) == SHAPE
+    assert L.ns_orthogonalize_batched(p, p + (1 << 30), 2, 64, 64, 0, 3.4445, -4.775, 2.0315, 1e-7, ws, need, None) == VALUE
+    assert L.ns_orthogonalize_batched(p, p + (1 << 30), 2, 64, 64, 5, math.inf, -4.775, 2.0315, 1e-7, ws, need, None) == VALUE
+    assert L.ns_orthogonalize_batched(p, p + (1 << 30), 2, 64, 64, 5, 3.4445, -4.775, 2.0315, 1e-7, ws, need - 1, None) == WORKSPACE
+    assert L.ns_orthogonalize_batched(p, p + 16, 2, 64, 64, 5, 3.4445, -4.775, 2.0315, 1e-7, ws, need, None) == ALIAS
+    assert L.ns_orthogonalize_batched(p, p + (1 << 30), 2, 64, 64, 5, 3.4445, -4.775, 2.0315, 1e-7, p + 256, need, None) == ALIAS
+    assert L.ns_orthogonalize_batched(p + 2, p + (1 << 30), 2, 64, 64, 5, 3.4445, -4.775, 2.0315, 1e-7, ws, need, None) == ALIGN
+    # apply
+    assert L.mp_apply_update(None, p, p, 1, 64, 0.02, 0.9998, None, None) == NULL
+    assert L.mp_apply_update(p, p + (1 << 30), p + (2 << 30), 1, 0, 0.02, 0.9998, None, None) == SHAPE
+    assert L.mp_apply_update(p, p + (1 << 30), p + (2 << 30), 1, 64, math.nan, 0.9998, None, None) == VALUE
+    assert L.mp_apply_update(p, p + 32, p + (2 << 30), 1, 64, 0.02, 0.9998, None, None) == ALIAS
+    assert L.mp_apply_update(p, p + (1 << 30), p + (2 << 30), 1, 64, 0.02, 0.9998, p + (3 << 30) + 2, None) == ALIGN
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch):
+    monkeypatch.setattr(api, "LIB_PATH", "/nonexistent/libmuonbank.so")
+    monkeypatch.setattr(api, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        api.lib()

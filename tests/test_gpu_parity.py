@@ -1,0 +1,178 @@
+"""GPU (HIP, through the C ABI) against the CPU oracle, stage by stage.
+
+Bars: bit-exact for momentum/u (both sides round the exact value once), for
+the mantissa split/recombine and for the apply (both sides compute
+RN32(RN32(w*d) - eta*v) exactly); relative Frobenius error <= 3e-2 per slot
+for the bf16 Newton-Schulz output against the fp64 oracle on the same bf16
+input; dead slots exactly zero.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from newton_schulz_bank_amd import api
+from newton_schulz_bank_amd.workloads import conditioned_bf16_matrices, make_random_bank, random_bf16_matrices
+from tests.gpu_util import bits, rel_fro, to_dev, vals
+
+pytestmark = pytest.mark.gpu
+
+NS_TOL = 3e-2
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    api.lib()
+
+
+# ---------------------------------------------------------------------------
+# apply
+# ---------------------------------------------------------------------------
+
+APPLY_SHAPES = [(3, 64, 64), (2, 37, 11), (1, 1, 12), (5, 128, 200), (40, 768, 768)]
+
+
+@pytest.mark.parametrize("shape", APPLY_SHAPES)
+@pytest.mark.parametrize("per_slot", [False, True])
+def test_apply_bit_exact(shape, per_slot):
+    say(f"apply {shape} per_slot={per_slot}")
+    rng = np.random.default_rng(sum(shape) + per_slot)
+    w = rng.normal(0, 0.02, shape).astype(np.float32)
+    hi, lo = oracle.split(w.view(np.uint32))
+    v64 = oracle.round_to_bf16(rng.normal(0, 0.04, shape))
+    v = oracle.f64_to_bf16_bits(v64)
+    sc = oracle.step_scalars(0.02, 0.01, 0.95, shape[1], shape[2])
+    per = rng.uniform(0.5, 2.0, shape[0]).astype(np.float32) if per_slot else None
+    eta = oracle.round_to_f32(sc.eta * per.astype(np.float64))[:, None, None] if per_slot else sc.eta
+    want_hi, want_lo = oracle.mp_apply_update(hi, lo, v64, eta, sc.decay)
+    d_hi, d_lo, d_v = to_dev(hi), to_dev(lo), to_dev(v)
+    api.mp_apply_update(d_hi, d_lo, d_v, sc.eta, sc.decay, to_dev(per) if per_slot else None)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(d_hi), want_hi)
+    np.testing.assert_array_equal(bits(d_lo), want_lo)
+
+
+def test_apply_edge_patterns():
+    """Carry across the 16-bit seam, subnormal weights, cancellation, zeros."""
+    say("apply edge patterns")
+    rng = np.random.default_rng(5)
+    n = 4096
+    hi = np.concatenate([np.full(1024, 0x3F80), rng.integers(0, 0x80, 1024), rng.integers(0, 0x8000, 1024),
+                         np.zeros(1024)]).astype(np.uint16)
+    lo = np.concatenate([np.full(1024, 0xFFFF), rng.integers(0, 65536, 2048), np.zeros(1024)]).astype(np.uint16)
+    v64 = np.concatenate([-oracle.round_to_bf16(np.abs(rng.normal(0, 1, 1024))),
+                          oracle.round_to_bf16(rng.normal(0, 1e-39, 1024)),
+                          oracle.round_to_bf16(rng.normal(0, 0.05, 1024)), np.zeros(1024)])
+    # cancellation block: w = eta*v/decay rounded, in the third quarter
+    sc = oracle.step_scalars(0.02, 0.01, 0.95, 3072, 768)
+    wc = (np.float64(sc.eta) * v64[2048:3072] / sc.decay).astype(np.float32)
+    hi[2048:3072], lo[2048:3072] = oracle.split(wc.view(np.uint32))
+    v = oracle.f64_to_bf16_bits(v64)
+    want = oracle.mp_apply_update(hi, lo, v64, sc.eta, sc.decay)
+    d_hi, d_lo = to_dev(hi.reshape(1, 1, n)), to_dev(lo.reshape(1, 1, n))
+    api.mp_apply_update(d_hi, d_lo, to_dev(v.reshape(1, 1, n)), sc.eta, sc.decay)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(d_hi).ravel(), want[0])
+    np.testing.assert_array_equal(bits(d_lo).ravel(), want[1])
+    assert np.all(bits(d_hi).ravel()[3072:] == 0) and np.all(bits(d_lo).ravel()[3072:] == 0)
+
+
+# ---------------------------------------------------------------------------
+# momentum + Nesterov
+# ---------------------------------------------------------------------------
+
+MOM_CASES = [((4, 256, 256), "f32"), ((3, 64, 64), "f32"), ((5, 33, 17), "bf16"), ((2, 128, 96), "bf16"),
+             ((3, 7, 5), "f32"), ((40, 768, 768), "bf16")]
+
+
+@pytest.mark.parametrize("shape,dtype", MOM_CASES)
+def test_momentum_bit_exact(shape, dtype):
+    say(f"momentum {shape} {dtype}")
+    scale = 1.0 if dtype == "f32" else 1e-3
+    bank = make_random_bank(sum(shape), *shape, grad_dtype=dtype, grad_scale=scale, mom_scale=scale)
+    sc = oracle.step_scalars(0.02, 0.01, 0.95, shape[1], shape[2])
+    want_buf, want_u = oracle.momentum_nesterov(vals(bank["grad"]), vals(bank["momentum"]), sc.mu, sc.nu,
+                                                oracle.F32 if dtype == "f32" else oracle.BF16)
+    bf = dtype == "bf16"
+    g, m = to_dev(bank["grad"], bf), to_dev(bank["momentum"], bf)
+    u = torch.empty(shape, dtype=torch.int16, device="cuda")
+    api.muon_momentum_update(g, m, u, sc.mu, sc.nu)
+    torch.cuda.synchronize()
+    got_buf = m.cpu().numpy().astype(np.float64) if dtype == "f32" else vals(bits(m))
+    np.testing.assert_array_equal(got_buf, want_buf)
+    np.testing.assert_array_equal(vals(bits(u)), want_u)
+
+
+# ---------------------------------------------------------------------------
+# Newton-Schulz
+# ---------------------------------------------------------------------------
+
+NS_SHAPES = [(4, 256, 256), (3, 100, 260), (3, 260, 100), (2, 130, 130), (2, 64, 512), (2, 512, 64),
+             (2, 1, 12), (3, 6, 12), (2, 12, 6), (2, 768, 768), (1, 3072, 768), (1, 768, 3072), (1, 1024, 1024),
+             (1, 200, 8), (2, 257, 129)]
+
+
+@pytest.mark.parametrize("shape", NS_SHAPES)
+def test_ns_parity(shape):
+    say(f"ns {shape}")
+    x = random_bf16_matrices(1 + sum(shape), *shape, scale=1e-3)
+    want = oracle.newton_schulz(vals(x))
+    y = api.ns_orthogonalize_batched(to_dev(x))
+    torch.cuda.synchronize()
+    got = vals(bits(y))
+    err = rel_fro(got, want)
+    say(f"  rel err per slot: {np.array2string(err, precision=4)}")
+    assert np.all(err <= NS_TOL), err
+
+
+def test_ns_zero_slot_and_determinism():
+    say("ns zero slot / determinism")
+    x = random_bf16_matrices(3, 4, 256, 384, scale=1.0)
+    x[2] = 0
+    dx = to_dev(x)
+    y1 = bits(api.ns_orthogonalize_batched(dx))
+    y2 = bits(api.ns_orthogonalize_batched(dx))
+    torch.cuda.synchronize()
+    assert np.all(y1[2] == 0)
+    np.testing.assert_array_equal(y1, y2)
+
+
+def test_ns_in_place():
+    say("ns in place")
+    x = random_bf16_matrices(4, 2, 128, 192)
+    for steps in (5, 1):
+        dx = to_dev(x)
+        ref = bits(api.ns_orthogonalize_batched(dx, steps=steps))
+        api.ns_orthogonalize_batched(dx, dx, steps=steps)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(dx), ref)
+
+
+def test_ns_band_on_well_conditioned_inputs():
+    """Singular values of the output lie in the iteration's fixed band [0.6818, 1.1344], widened by 0.03."""
+    say("ns band")
+    for shape in [(4, 256, 256), (2, 128, 384), (2, 384, 128)]:
+        x = conditioned_bf16_matrices(sum(shape), *shape)
+        got = vals(bits(api.ns_orthogonalize_batched(to_dev(x))))
+        for i in range(shape[0]):
+            sv = np.linalg.svd(got[i], compute_uv=False)
+            assert sv.min() >= 0.6818 - 0.03 and sv.max() <= 1.1344 + 0.03, (shape, sv.min(), sv.max())
+
+
+def test_ns_transpose_equivariance():
+    say("ns transpose equivariance")
+    x = random_bf16_matrices(8, 3, 192, 320)
+    y = vals(bits(api.ns_orthogonalize_batched(to_dev(x))))
+    xt = np.ascontiguousarray(x.transpose(0, 2, 1))
+    yt = vals(bits(api.ns_orthogonalize_batched(to_dev(xt))))
+    assert np.all(rel_fro(yt.transpose(0, 2, 1), y) <= NS_TOL)

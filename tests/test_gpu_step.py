@@ -1,0 +1,131 @@
+"""The whole Muon bank step on the five workloads, through muon_bank_step.
+
+Stage isolation: the oracle's momentum runs on the same inputs (bit-exact
+buf' and u), the oracle's Newton-Schulz on the GPU's u (tolerance), and the
+oracle's apply on the GPU's v (bit-exact weights), so no stage's tolerance
+leaks into the next.  End to end, the weights agree within one fp32 ulp plus
+eta times the difference of the two v.  The big workloads are checked on
+sampled slots (plus every dead slot); the launch configuration is the one the
+benchmark times.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from newton_schulz_bank_amd import api
+from newton_schulz_bank_amd.workloads import CONFIGS, make_bank
+from tests.gpu_util import bits, rel_fro, to_dev, vals
+
+pytestmark = pytest.mark.gpu
+
+NS_TOL = 3e-2
+# slots checked element by element (None = all) and slots whose NS is recomputed by the oracle
+SAMPLES = {
+    0: {"elem": None, "ns": {0: [0, 1, 2, 3]}},
+    1: {"elem": None, "ns": {0: [0, 21, 39]}},
+    2: {"elem": None, "ns": {0: [0, 22]}},
+    3: {"elem": None, "ns": {0: [5], 1: [11], 2: [0], 3: [0, 9]}},
+    4: {"elem": {0: [0, 95], 1: [0, 47], 2: [0, 13, 14, 15, 23]}, "ns": {0: [50], 1: [7], 2: [13]}},
+}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _run(config):
+    specs = CONFIGS[config]
+    host, banks = [], []
+    for i, spec in enumerate(specs):
+        h = make_bank(config, i)
+        bf = spec.grad_dtype == "bf16"
+        b = api.Bank(grad=to_dev(h["grad"], bf), momentum=to_dev(h["momentum"], bf), w_hi=to_dev(h["w_hi"]),
+                     w_lo=to_dev(h["w_lo"]))
+        b.v_out = torch.empty(h["w_hi"].shape, dtype=torch.int16, device="cuda")
+        b.u_out = torch.empty(h["w_hi"].shape, dtype=torch.int16, device="cuda")
+        host.append(h)
+        banks.append(b)
+    api.muon_bank_step(banks)
+    torch.cuda.synchronize()
+    return specs, host, banks
+
+
+@pytest.mark.parametrize("config", [0, 1, 2, 3, 4])
+def test_bank_step_matches_oracle(config):
+    say(f"bank step config {config}")
+    specs, host, banks = _run(config)
+    samp = SAMPLES[config]
+    for bi, (spec, h, b) in enumerate(zip(specs, host, banks)):
+        elem = list(range(spec.batch)) if samp["elem"] is None else samp["elem"][bi]
+        storage = oracle.F32 if spec.grad_dtype == "f32" else oracle.BF16
+        sc = oracle.step_scalars(0.02, 0.01, 0.95, spec.rows, spec.cols)
+        g = vals(h["grad"][elem])
+        m = vals(h["momentum"][elem])
+        want_buf, want_u = oracle.momentum_nesterov(g, m, sc.mu, sc.nu, storage)
+        got_buf = (b.momentum.float().cpu().numpy()[elem].astype(np.float64) if storage == oracle.F32
+                   else vals(bits(b.momentum)[elem]))
+        np.testing.assert_array_equal(got_buf, want_buf, err_msg=f"{spec.name} momentum")
+        u_gpu = bits(b.u_out)
+        np.testing.assert_array_equal(vals(u_gpu[elem]), want_u, err_msg=f"{spec.name} u")
+        v_gpu = bits(b.v_out)
+        # apply on the GPU's v: bit-exact
+        want_hi, want_lo = oracle.mp_apply_update(h["w_hi"][elem], h["w_lo"][elem], vals(v_gpu[elem]), sc.eta,
+                                                  sc.decay)
+        np.testing.assert_array_equal(bits(b.w_hi)[elem], want_hi, err_msg=f"{spec.name} w_hi")
+        np.testing.assert_array_equal(bits(b.w_lo)[elem], want_lo, err_msg=f"{spec.name} w_lo")
+        # dead slots stay exactly zero everywhere
+        for s in spec.dead_slots:
+            assert np.all(bits(b.momentum)[s] == 0) if storage == oracle.BF16 else True
+            assert np.all(v_gpu[s] == 0) and np.all(u_gpu[s] == 0), f"{spec.name} dead slot {s}"
+            assert np.all(bits(b.w_hi)[s] == 0) and np.all(bits(b.w_lo)[s] == 0)
+        # Newton-Schulz on the GPU's u
+        ns_slots = samp["ns"].get(bi, [])
+        if ns_slots:
+            want_v = oracle.newton_schulz(vals(u_gpu[ns_slots]))
+            err = rel_fro(vals(v_gpu[ns_slots]), want_v)
+            say(f"  {spec.name} NS rel err {np.array2string(err, precision=4)}")
+            assert np.all(err <= NS_TOL), err
+            # end to end on those slots: |w_gpu - w_or| <= 1 ulp + eta |v_gpu - v_or|
+            v_or = oracle.round_to_bf16(want_v)
+            or_hi, or_lo = oracle.mp_apply_update(h["w_hi"][ns_slots], h["w_lo"][ns_slots], v_or, sc.eta, sc.decay)
+            w_or = oracle.recombine(or_hi, or_lo).view(np.float32).astype(np.float64)
+            w_gp = oracle.recombine(bits(b.w_hi)[ns_slots], bits(b.w_lo)[ns_slots]).view(np.float32).astype(np.float64)
+            ulp = np.abs(np.spacing(w_or.astype(np.float32))).astype(np.float64)
+            bound = ulp + sc.eta * np.abs(vals(v_gpu[ns_slots]) - v_or) * (1 + 1e-6)
+            assert np.all(np.abs(w_gp - w_or) <= bound)
+
+
+def test_bank_step_is_deterministic():
+    say("bank step determinism")
+    outs = []
+    for _ in range(2):
+        specs, host, banks = _run(1)
+        outs.append([(bits(b.w_hi), bits(b.w_lo), bits(b.v_out)) for b in banks])
+    for a, b in zip(outs[0], outs[1]):
+        for x, y in zip(a, b):
+            np.testing.assert_array_equal(x, y)
+
+
+def test_per_slot_lr_and_multipliers():
+    say("bank step per-slot lr")
+    h = make_bank(1, 0, slots=list(range(6)))
+    per = np.array([1.0, 0.5, 2.0, 1.0, 0.25, 3.0], dtype=np.float32)
+    b = api.Bank(grad=to_dev(h["grad"], True), momentum=to_dev(h["momentum"], True), w_hi=to_dev(h["w_hi"]),
+                 w_lo=to_dev(h["w_lo"]), lr_mul=1.5, wd_mul=2.0, lr_mul_per_slot=to_dev(per))
+    b.v_out = torch.empty(h["w_hi"].shape, dtype=torch.int16, device="cuda")
+    hp = api.make_hparams(lr=0.05, weight_decay=0.1, momentum=0.9)
+    api.muon_bank_step([b], hp)
+    torch.cuda.synchronize()
+    sc = oracle.step_scalars(0.05, 0.1, 0.9, 768, 768, lr_mul=1.5, wd_mul=2.0)
+    eta = oracle.round_to_f32(sc.eta * per.astype(np.float64))[:, None, None]
+    v = vals(bits(b.v_out))
+    want_hi, want_lo = oracle.mp_apply_update(h["w_hi"], h["w_lo"], v, eta, sc.decay)
+    np.testing.assert_array_equal(bits(b.w_hi), want_hi)
+    np.testing.assert_array_equal(bits(b.w_lo), want_lo)
+    want_buf, _ = oracle.momentum_nesterov(vals(h["grad"]), vals(h["momentum"]), sc.mu, sc.nu, oracle.BF16)
+    np.testing.assert_array_equal(vals(bits(b.momentum)), want_buf)
