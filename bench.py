@@ -1,0 +1,277 @@
+"""Benchmark of the Muon bank step on one MI355X.
+
+One step = one full pass of the hot path over the bank: momentum + Nesterov,
+Frobenius pre-scale, five quintic Newton-Schulz rounds (Gram, polynomial,
+update contractions on bf16 MFMA), and the mixed-precision apply.  Inputs
+are seeded synthetic banks (no dataset), resident in HBM before the timed
+region.  The default workload is the attention QKVO bank (10, 3072, 768)
+viewed as (40, 768, 768).
+
+Prints one JSON line.  ``value`` is the step's throughput in algorithmic
+Newton-Schulz TFLOP/s: live slots x 5*(m(m+1)n + m^2(m+1) + 2m^2 n) per
+step (symmetric Gram and A*A counted once) / wall time of the whole step.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+METRIC = "Muon bank-step ms and NS TFLOP/s (% bf16 MFMA peak), 1×MI355X"
+PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 bf16 flop/clk/CU (dense)
+PEAK_HBM_GBPS = 8000.0
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def ns_flops_per_slot(rows: int, cols: int, steps: int = 5) -> dict:
+    m, n = min(rows, cols), max(rows, cols)
+    return {"ns_gram": steps * m * (m + 1) * n, "ns_poly": steps * m * m * (m + 1), "ns_update": steps * 2 * m * m * n}
+
+
+def bank_bytes(spec) -> dict:
+    numel = spec.batch * spec.rows * spec.cols
+    g = 4 if spec.grad_dtype == "f32" else 2
+    return {"momentum": numel * (g + 2 * g + 2), "apply": numel * 10}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", type=int, default=1, help="workload id 0..4 (1 = attention bank, the metric's case)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-parity", action="store_true")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the bank step is measured on a single MI355X; "
+                          "--gpus must be 1"}), flush=True)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU (HIP device)")
+    sys.path.insert(0, HERE)
+    from newton_schulz_bank_amd import api
+    from newton_schulz_bank_amd.workloads import CONFIG_NAMES, CONFIGS, make_bank
+
+    api.lib()    # fails loudly if libmuonbank.so is missing
+    specs = CONFIGS[args.config]
+    hosts = [make_bank(args.config, i) for i in range(len(specs))]
+
+    def upload():
+        banks = []
+        for spec, h in zip(specs, hosts):
+            bf = spec.grad_dtype == "bf16"
+
+            def dev(a, as_bf16=False):
+                t = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+                return t.view(torch.bfloat16) if as_bf16 and a.dtype == np.uint16 else t
+            banks.append(api.Bank(grad=dev(h["grad"], bf), momentum=dev(h["momentum"], bf), w_hi=dev(h["w_hi"]),
+                                  w_lo=dev(h["w_lo"])))
+        return banks
+
+    banks = upload()
+    ws = torch.empty(api.mb_step_workspace_bytes(banks), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    # ---- parity gate on a sample (the full checks live in the test suite)
+    parity = None
+    if not args.no_parity:
+        parity = parity_check(api, specs, hosts, args.config)
+
+    # ---- timed region
+    for _ in range(args.warmup):
+        api.muon_bank_step(banks, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        api.muon_bank_step(banks, workspace=ws, stream=stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = start.elapsed_time(stop) / args.steps
+
+    # ---- per-kernel durations with HIP events on the launch stream (a second timed pass)
+    api.mb_timing_enable(True)
+    api.mb_timing_read()
+    for _ in range(args.steps):
+        api.muon_bank_step(banks, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    per_kernel = api.mb_timing_read()
+    api.mb_timing_enable(False)
+
+    live_slots = sum(len(s.live_slots) for s in specs)
+    alg = {"ns_gram": 0, "ns_poly": 0, "ns_update": 0}
+    for s in specs:
+        f = ns_flops_per_slot(s.rows, s.cols)
+        for k in alg:
+            alg[k] += f[k] * len(s.live_slots)
+    ns_flops = sum(alg.values())
+    bytes_ = {"momentum": sum(bank_bytes(s)["momentum"] for s in specs),
+              "apply": sum(bank_bytes(s)["apply"] for s in specs)}
+
+    kernels = {}
+    for name, (n, tot) in per_kernel.items():
+        per_launch = tot / n
+        kernels[name] = {"launches_per_step": n / args.steps, "avg_us": per_launch * 1e3, "ms_per_step": tot / args.steps}
+    ns_ms = sum(kernels.get(k, {"ms_per_step": 0})["ms_per_step"] for k in alg)
+    for k in alg:
+        if k in kernels:
+            flops_per_launch = alg[k] / kernels[k]["launches_per_step"]
+            kernels[k]["alg_tflops"] = flops_per_launch / (kernels[k]["avg_us"] * 1e-6) / 1e12
+    for k in ("momentum", "apply"):
+        if k in kernels:
+            b = bytes_[k] / kernels[k]["launches_per_step"]
+            kernels[k]["gbps"] = b / (kernels[k]["avg_us"] * 1e-6) / 1e9
+
+    dominant = max(alg, key=lambda k: kernels.get(k, {"ms_per_step": 0})["ms_per_step"])
+    achieved = kernels[dominant]["alg_tflops"]
+    roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": read_traffic(dominant, args.config)}
+
+    value = ns_flops / (ms_per_step * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": CONFIG_NAMES[args.config], "config_id": args.config,
+                   "banks": [[s.batch, s.rows, s.cols] for s in specs], "live_slots": live_slots,
+                   "ns_steps": 5, "grad_dtype": specs[0].grad_dtype},
+        "matrices_per_s": round(live_slots / (ms_per_step * 1e-3), 1),
+        "ns_ms_per_step": round(ns_ms, 4),
+        "ns_tflops": round(ns_flops / (ns_ms * 1e-3) / 1e12, 2) if ns_ms > 0 else None,
+        "ns_frac_of_peak": round(ns_flops / (ns_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4) if ns_ms > 0 else None,
+        "apply_gbps": round(kernels.get("apply", {}).get("gbps", 0.0), 1),
+        "apply_frac_of_hbm": round(kernels.get("apply", {}).get("gbps", 0.0) / PEAK_HBM_GBPS, 4),
+        "momentum_gbps": round(kernels.get("momentum", {}).get("gbps", 0.0), 1),
+        "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kernels.items()},
+        "wall_s_timed": round(wall, 4),
+        "roofline": roofline,
+        "parity": parity,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(specs, hosts, args.config)
+    print(json.dumps(out), flush=True)
+
+
+def parity_check(api, specs, hosts, config):
+    """One step on fresh copies of the inputs; sampled slots against the oracle."""
+    import torch
+    sys.path.insert(0, HERE)
+    import oracle
+    bi = 0
+    spec, h = specs[bi], hosts[bi]
+    slot = spec.live_slots[0]
+    bf = spec.grad_dtype == "bf16"
+    sl = lambda a: np.ascontiguousarray(a[slot:slot + 1])
+
+    def dev(a, as_bf16=False):
+        t = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+        return t.view(torch.bfloat16) if as_bf16 and a.dtype == np.uint16 else t
+    b = api.Bank(grad=dev(sl(h["grad"]), bf), momentum=dev(sl(h["momentum"]), bf), w_hi=dev(sl(h["w_hi"])),
+                 w_lo=dev(sl(h["w_lo"])))
+    b.v_out = torch.empty(b.w_hi.shape, dtype=torch.int16, device="cuda")
+    api.muon_bank_step([b])
+    torch.cuda.synchronize()
+    vals = (lambda a: a.astype(np.float64)) if not bf else oracle.bf16_bits_to_f64
+    ref = oracle.muon_bank_step(vals(sl(h["grad"])), vals(sl(h["momentum"])), sl(h["w_hi"]), sl(h["w_lo"]),
+                                oracle.F32 if not bf else oracle.BF16)
+    v = oracle.bf16_bits_to_f64(b.v_out.cpu().numpy().view(np.uint16))
+    err = float(np.linalg.norm(v - ref["v64"]) / max(np.linalg.norm(ref["v64"]), 1e-30))
+    w_hi_bits = b.w_hi.cpu().numpy().view(np.uint16)
+    w_lo_bits = b.w_lo.cpu().numpy().view(np.uint16)
+    want = oracle.mp_apply_update(sl(h["w_hi"]), sl(h["w_lo"]), v, ref["scalars"].eta, ref["scalars"].decay)
+    ok_apply = bool(np.array_equal(w_hi_bits, want[0]) and np.array_equal(w_lo_bits, want[1]))
+    mom = b.momentum.float().cpu().numpy().astype(np.float64) if not bf else oracle.bf16_bits_to_f64(
+        b.momentum.view(torch.int16).cpu().numpy().view(np.uint16))
+    ok_mom = bool(np.array_equal(mom, ref["momentum"]))
+    if not (ok_apply and ok_mom and err <= 3e-2):
+        raise SystemExit(f"parity failure on {spec.name} slot {slot}: ns rel err {err}, apply {ok_apply}, "
+                         f"momentum {ok_mom}")
+    return {"bank": spec.name, "slot": slot, "ns_rel_fro_err": round(err, 5), "apply_bit_exact": ok_apply,
+            "momentum_bit_exact": ok_mom}
+
+
+def cpu_baseline(specs, hosts, config):
+    """The oracle as it stands, on a bounded sample of the same workload, on the host's cores."""
+    sys.path.insert(0, HERE)
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info() if t.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    budget_s = 12.0
+    flops, elapsed, desc = 0, 0.0, []
+    for spec, h in zip(specs, hosts):
+        live = list(spec.live_slots)
+        take = []
+        for s in live:
+            take.append(s)
+            if elapsed >= budget_s:
+                break
+            sl = np.ascontiguousarray
+            bf = spec.grad_dtype == "bf16"
+            vals = (lambda a: a.astype(np.float64)) if not bf else oracle.bf16_bits_to_f64
+            t0 = time.perf_counter()
+            oracle.muon_bank_step(vals(sl(h["grad"][s:s + 1])), vals(sl(h["momentum"][s:s + 1])),
+                                  sl(h["w_hi"][s:s + 1]), sl(h["w_lo"][s:s + 1]), oracle.F32 if not bf else oracle.BF16)
+            elapsed += time.perf_counter() - t0
+            f = ns_flops_per_slot(spec.rows, spec.cols)
+            flops += sum(f.values())
+        desc.append(f"{len(take)} of {len(live)} live slots of {spec.name} ({spec.rows}x{spec.cols})")
+        if elapsed >= budget_s:
+            break
+    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": "full oracle step (momentum, fp64 NS5, exact apply) on " + "; ".join(desc),
+            "seconds": round(elapsed, 2), "host": platform.processor() or platform.machine()}
+
+
+def read_traffic(kernel: str, config: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(HERE, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+        entry = data.get(f"{kernel}:config{config}")
+        if not entry:
+            return None
+        import hashlib
+        src = open(os.path.join(HERE, "newton_schulz_bank_amd", "csrc", entry["source"]), "rb").read()
+        if hashlib.sha256(src).hexdigest() != entry["source_sha256"]:
+            return None
+        return entry["bytes_per_launch"]
+    except Exception:
+        return None
+
+
+if __name__ == "__main__":
+    main()
