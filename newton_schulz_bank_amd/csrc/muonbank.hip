@@ -67,6 +67,45 @@ struct Timer final : mb::RoundTimer {
 };
 
 // ---------------------------------------------------------------------------
+// side streams: a bank can be cut into slot groups that run on library-owned
+// streams, forked from and joined back to the caller's stream with events.
+// Measured on MI355X, kernels on separate streams barely overlap (average
+// concurrency 1.13 with four groups, and a slower step), so one lane is used:
+// every unit then runs on the caller's stream.
+// ---------------------------------------------------------------------------
+
+constexpr int kLanes = 1;
+
+struct DeviceStreams {
+    bool ready = false;
+    hipStream_t side[kLanes];
+    hipEvent_t fork;
+    hipEvent_t done[kLanes];
+};
+
+std::mutex g_streams_mu;
+DeviceStreams g_streams[64];
+
+// The calling thread's current device's pool, created on first use (default priority).
+hipError_t device_streams(DeviceStreams** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    DeviceStreams& d = g_streams[dev];
+    if (!d.ready) {
+        for (int i = 0; i < kLanes; ++i) {
+            if ((e = hipStreamCreateWithFlags(&d.side[i], hipStreamNonBlocking)) != hipSuccess) return e;
+            if ((e = hipEventCreateWithFlags(&d.done[i], hipEventDisableTiming)) != hipSuccess) return e;
+        }
+        if ((e = hipEventCreateWithFlags(&d.fork, hipEventDisableTiming)) != hipSuccess) return e;
+        d.ready = true;
+    }
+    *out = &d;
+    return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
 // validation helpers
 // ---------------------------------------------------------------------------
 
@@ -85,6 +124,12 @@ mb_status check_shape(int64_t batch, int64_t rows, int64_t cols, const char* wha
     const int64_t slot = rows * cols;      // < 2^60
     if (slot > ((int64_t)1 << 62) / batch)
         return fail(MB_ERR_SHAPE, "%s: element count overflows", what);
+    // the contraction grids enumerate batch x 128x128 output tiles in 32-bit indices
+    const int64_t m = rows < cols ? rows : cols, n = rows < cols ? cols : rows;
+    const int64_t tiles = ((m + 127) / 128) * ((n + 127) / 128);
+    if (tiles > ((int64_t)1 << 30) / batch)
+        return fail(MB_ERR_SHAPE, "%s: shape (%lld, %lld, %lld) has too many 128x128 tiles", what, (long long)batch,
+                    (long long)rows, (long long)cols);
     return MB_OK;
 }
 
@@ -360,49 +405,101 @@ mb_status muon_bank_step(const mb_bank* banks, int32_t num_banks, const mb_hpara
     s = check_no_overlap(ranges);
     if (s != MB_OK) return s;
 
-    // ---- enqueue
+    // ---- enqueue: every bank is cut into up to kLanes contiguous slot groups (small banks stay
+    // whole); group g of the call runs on side stream g % kLanes
     hipStream_t st = (hipStream_t)stream;
-    Timer timer;
-    char* ws = (char*)workspace;
+    struct Unit {
+        int32_t bank;
+        int64_t s0, s1;
+    };
+    std::vector<Unit> units;
     for (int32_t i = 0; i < num_banks; ++i) {
         const mb_bank& b = banks[i];
+        const bool big = b.rows * b.cols >= 65536 && b.batch >= 2 * kLanes;
+        const int64_t groups = big ? kLanes : 1;
+        for (int64_t g = 0; g < groups; ++g)
+            units.push_back({i, b.batch * g / groups, b.batch * (g + 1) / groups});
+    }
+    std::lock_guard<std::mutex> lk(g_streams_mu);
+    DeviceStreams* ds = nullptr;
+    const bool fork = units.size() > 1;
+    if (fork) {
+        hipError_t e = device_streams(&ds);
+        if (e != hipSuccess) return fail(MB_ERR_HIP, "side streams: %s", hipGetErrorString(e));
+        if ((e = hipEventRecord(ds->fork, st)) != hipSuccess) return fail(MB_ERR_HIP, "fork: %s", hipGetErrorString(e));
+        for (int l = 0; l < kLanes; ++l)
+            if ((e = hipStreamWaitEvent(ds->side[l], ds->fork, 0)) != hipSuccess)
+                return fail(MB_ERR_HIP, "fork: %s", hipGetErrorString(e));
+    }
+    Timer timer;
+    char* ws = (char*)workspace;
+    std::vector<size_t> bank_off(num_banks);
+    {
+        size_t off = 0;
+        for (int32_t i = 0; i < num_banks; ++i) {
+            bank_off[i] = off;
+            off += bank_ws_layout(banks[i].batch, banks[i].rows, banks[i].cols, (banks[i].rows * banks[i].cols) % 8 == 0).total;
+        }
+    }
+    for (size_t ui = 0; ui < units.size(); ++ui) {
+        const Unit& un = units[ui];
+        const mb_bank& b = banks[un.bank];
+        hipStream_t us = fork ? ds->side[ui % kLanes] : st;
         const int64_t slot = b.rows * b.cols;
+        const int64_t m = b.rows < b.cols ? b.rows : b.cols;
         const bool vec = slot % 8 == 0;
+        const int nch = mb::stream_chunks(slot, vec);
         const BankWs L = bank_ws_layout(b.batch, b.rows, b.cols, vec);
+        char* bw = ws + bank_off[un.bank];
+        const int64_t s0 = un.s0, nb = un.s1 - un.s0;
         // host scalars in double, rounded once to float32
         const float mu = f32(hp.momentum);
         const float nu = f32(1.0 - hp.momentum);
         const float decay = f32(1.0 - hp.lr * hp.weight_decay * b.wd_mul);
         const float eta = f32(hp.lr * std::sqrt(std::max(1.0, (double)b.rows / (double)b.cols)) * b.lr_mul);
 
-        uint16_t* u = b.u_out ? b.u_out : (uint16_t*)(ws + L.u);
-        uint16_t* v = b.v_out ? b.v_out : (uint16_t*)(ws + L.u);   // u is dead once the first round has read it
-        float* partials = (float*)(ws + L.partials);
-        float* scale = (float*)(ws + L.scale);
-        int* live = (int*)(ws + L.live);
+        const size_t gsz = b.grad_dtype == MB_F32 ? 4 : 2;
+        const void* grad = (const char*)b.grad + s0 * slot * gsz;
+        void* mom = (char*)b.momentum + s0 * slot * gsz;
+        uint16_t* w_hi = b.w_hi + s0 * slot;
+        uint16_t* w_lo = b.w_lo + s0 * slot;
+        const float* lrm = b.lr_mul_per_slot ? b.lr_mul_per_slot + s0 : nullptr;
+        uint16_t* u = (b.u_out ? b.u_out : (uint16_t*)(bw + L.u)) + s0 * slot;
+        uint16_t* v = (b.v_out ? b.v_out : (uint16_t*)(bw + L.u)) + s0 * slot;   // u is dead once round 1 read it
+        uint16_t* x1 = (uint16_t*)(bw + L.x1) + s0 * slot;
+        uint16_t* x2 = (uint16_t*)(bw + L.x2) + s0 * slot;
+        uint16_t* A = (uint16_t*)(bw + L.A) + s0 * m * m;
+        uint16_t* Bm = (uint16_t*)(bw + L.Bm) + s0 * m * m;
+        float* partials = (float*)(bw + L.partials) + s0 * nch;
+        float* scale = (float*)(bw + L.scale) + s0;
+        int* live = (int*)(bw + L.live) + s0;
 
-        timer.begin("momentum", st);
-        hipError_t e = mb::launch_momentum(b.grad, b.momentum, u, partials, b.batch, slot, b.grad_dtype == MB_F32, vec,
-                                           mu, nu, st);
-        timer.end(st);
+        timer.begin("momentum", us);
+        hipError_t e = mb::launch_momentum(grad, mom, u, partials, nb, slot, b.grad_dtype == MB_F32, vec, mu, nu, us);
+        timer.end(us);
         if (e != hipSuccess) return fail(MB_ERR_HIP, "momentum launch: %s", hipGetErrorString(e));
-        timer.begin("ns_scale", st);
-        e = mb::launch_ns_scale(partials, mb::stream_chunks(slot, vec), b.batch, f32(hp.eps), scale, live, st);
-        timer.end(st);
+        timer.begin("ns_scale", us);
+        e = mb::launch_ns_scale(partials, nch, nb, f32(hp.eps), scale, live, us);
+        timer.end(us);
         if (e != hipSuccess) return fail(MB_ERR_HIP, "ns_scale launch: %s", hipGetErrorString(e));
         // with one round and no v_out, the round would read u while writing v in the same buffer
-        uint16_t* dest = (hp.ns_steps == 1 && v == u) ? (uint16_t*)(ws + L.x2) : v;
-        s = run_ns(u, dest, (uint16_t*)(ws + L.x1), (uint16_t*)(ws + L.x2), (uint16_t*)(ws + L.A),
-                   (uint16_t*)(ws + L.Bm), b.batch, b.rows, b.cols, hp.ns_steps, hp.a, hp.b, hp.c, scale, live, st,
-                   timer);
+        uint16_t* dest = (hp.ns_steps == 1 && v == u) ? x2 : v;
+        s = run_ns(u, dest, x1, x2, A, Bm, nb, b.rows, b.cols, hp.ns_steps, hp.a, hp.b, hp.c, scale, live, us, timer);
         if (s != MB_OK) return s;
-        timer.begin("apply", st);
-        e = mb::launch_apply(b.w_hi, b.w_lo, dest, b.batch, slot, vec, eta, decay, b.lr_mul_per_slot, st);
-        timer.end(st);
+        timer.begin("apply", us);
+        e = mb::launch_apply(w_hi, w_lo, dest, nb, slot, vec, eta, decay, lrm, us);
+        timer.end(us);
         if (e != hipSuccess) return fail(MB_ERR_HIP, "apply launch: %s", hipGetErrorString(e));
         if (dest != v) {
-            e = hipMemcpyAsync(v, dest, (size_t)(b.batch * slot) * 2, hipMemcpyDeviceToDevice, st);
+            e = hipMemcpyAsync(v, dest, (size_t)(nb * slot) * 2, hipMemcpyDeviceToDevice, us);
             if (e != hipSuccess) return fail(MB_ERR_HIP, "copy: %s", hipGetErrorString(e));
+        }
+    }
+    if (fork) {
+        for (int l = 0; l < kLanes; ++l) {
+            hipError_t e = hipEventRecord(ds->done[l], ds->side[l]);
+            if (e == hipSuccess) e = hipStreamWaitEvent(st, ds->done[l], 0);
+            if (e != hipSuccess) return fail(MB_ERR_HIP, "join: %s", hipGetErrorString(e));
         }
     }
     return ok();

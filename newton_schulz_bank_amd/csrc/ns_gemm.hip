@@ -25,6 +25,8 @@
 // off-diagonal tile is also written mirrored.  Slots with a zero norm are
 // skipped; the update writes zeros for them.
 
+#include <cmath>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -48,6 +50,7 @@ struct GemmArgs {
     uint16_t* out; int64_t ldo; int64_t o_stride;
     int M, N, K;
     int tiles_m, tiles_n;
+    int batch;
     float alpha, beta;          // GRAM: alpha; POLY: c, b; UPDATE: 1, a
     const float* scale;         // per-slot Frobenius scale (first round only), else null
     const int* live;            // per-slot live flag
@@ -137,16 +140,26 @@ __device__ __forceinline__ void sym_tile(int t, int T, int& I, int& J) {
 
 template <bool P_KMAJOR, bool Q_KMAJOR, int EPI, bool VEC>
 __global__ void __launch_bounds__(NT, 2) ns_gemm_kernel(GemmArgs args) {
-    const int slot = blockIdx.y;
+    // XCD-aware mapping: workgroups are dispatched round-robin over the 8 XCDs, so
+    // workgroup L runs on XCD L % 8.  Give XCD x the contiguous range
+    // [x*per, (x+1)*per) of the slot-major work list, so all tiles of a slot share
+    // one XCD's L2 and the operand panels they re-read stay cached there.
+    const int per_slot = (EPI == EPI_UPDATE) ? args.tiles_m * args.tiles_n : args.tiles_m * (args.tiles_m + 1) / 2;
+    const int total = args.batch * per_slot;
+    const int per_xcd = (total + 7) >> 3;
+    const int w = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+    if (w >= total) return;
+    const int slot = w / per_slot;
+    const int tile = w - slot * per_slot;
     if (!args.live[slot]) {
         if (EPI != EPI_UPDATE) return;
     }
     int ti, tj;
     if (EPI == EPI_UPDATE) {
-        ti = blockIdx.x / args.tiles_n;
-        tj = blockIdx.x % args.tiles_n;
+        ti = tile / args.tiles_n;
+        tj = tile % args.tiles_n;
     } else {
-        sym_tile(blockIdx.x, args.tiles_m, ti, tj);
+        sym_tile(tile, args.tiles_m, ti, tj);
     }
     const int i0 = ti * BM, j0 = tj * BN;
     const int tid = threadIdx.x;
@@ -284,11 +297,301 @@ __global__ void __launch_bounds__(NT, 2) ns_gemm_kernel(GemmArgs args) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Fast path for M, N multiples of the tile and K a multiple of 64 (every bank
+// shape).  Operand tiles are copied global -> LDS directly with MUBUF
+// buffer_load ... lds (16 B per lane) into a two-stage ring, so the copy of
+// stage k+1 overlaps the MFMAs of stage k with no register staging.  The LDS
+// layouts are XOR-swizzled so the 16-byte fragment reads and the transposing
+// reads hit distinct banks.  Tile shapes are template parameters: 128x128 with
+// four wavefronts (two workgroups per CU) or 256x256 with eight (one per CU,
+// twice the flops per byte moved out of L2).
+// ---------------------------------------------------------------------------
+
+// K-major tile [rows][8 chunks of 8 k]: chunk c of row R sits at entry R*8 + (c ^ ks(R)),
+// conflict-free for the 16 lanes a 16-byte read serves per cycle.
+__device__ __forceinline__ int ks(int R) { return (R & 7) ^ ((R >> 3) & 1); }
+// MN-major tile [64 k rows][rows/8 chunks of 8 mn]: chunk c of row k sits at entry
+// k*(rows/8) + (c ^ ms(k)).  A transposing read serves 32 lanes per cycle (4 k rows x 4
+// chunks x 2 halves), which the XOR with 4*(k & 3) spreads over all 64 banks.
+__device__ __forceinline__ int ms(int k) { return 4 * (k & 3); }
+
+// MUBUF load of 16 bytes per lane straight into LDS (lane l -> LDS base + 16*l).  Unlike the
+// FLAT-encoded global_load_lds it is tracked by vmcnt alone, so waiting for LDS reads never
+// waits for copies still in flight; reads past the descriptor's size return zeros.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+extern "C" __device__ void mb_raw_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) uint32_t* lds,
+                                                  int size, int voffset, int soffset, int offset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// Buffer descriptor of `bytes` bytes at `base` (raw buffer, stride 0; word 3 as for every gfx9 part).
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    i32x4 r;
+    r[0] = (int32_t)(uint32_t)a;
+    r[1] = (int32_t)(uint32_t)((a >> 32) & 0xFFFFu);
+    r[2] = (int32_t)bytes;
+    r[3] = 0x00020000;
+    return r;
+}
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int NW = WM * WN, NT = 64 * NW;
+    static constexpr int TM = BM / WM, TN = BN / WN;      // outputs per wavefront
+    static constexpr int FM = TM / 32, FN = TN / 32;      // 32x32 MFMA blocks per wavefront
+    static constexpr int STAGE = (BM + BN) * 64;          // elements per ring stage
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tiles are whole MFMA blocks");
+    static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "copy instructions split evenly");
+};
+using Cfg128 = Cfg<128, 128, 2, 2>;
+using Cfg256 = Cfg<256, 256, 2, 4>;
+
+// Copy one ROWS (mn) x 64 (k) operand tile into LDS: ROWS/8 instructions of 64 lanes x 16 B,
+// instruction q filling entries [64q, 64q + 64).
+template <bool KMAJOR, int ROWS, int NW>
+__device__ __forceinline__ void load_tile_lds(i32x4 rsrc, int ld, int mn0, int k0, uint16_t* lds, int wave,
+                                              int lane) {
+    constexpr int NI = ROWS / 8 / NW;
+    constexpr int CPR = ROWS / 8;                         // chunks per k row (MN-major)
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+        const int q = wave * NI + j;
+        int elem;
+        if (KMAJOR) {
+            const int R = q * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ ks(R);
+            elem = (mn0 + R) * ld + k0 + c * 8;
+        } else {
+            const int k = q * (64 / CPR) + lane / CPR;
+            const int c = (lane % CPR) ^ ms(k);
+            elem = (k0 + k) * ld + mn0 + c * 8;
+        }
+        mb_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) uint32_t*)(lds + q * 512), 16, elem * 2, 0, 0,
+                               0);
+    }
+}
+
+// MFMA fragment (32 rows x 16 k; lane l holds row l%32, k = kk*16 + 8*(l/32) + 0..7) from a swizzled tile.
+template <bool KMAJOR, int ROWS>
+__device__ __forceinline__ bf16x8 read_frag_fast(const uint16_t* lds, int mn_base, int kk, int lane) {
+    if (KMAJOR) {
+        const int R = mn_base + (lane & 31);
+        const int c = 2 * kk + (lane >> 5);
+        return *reinterpret_cast<const bf16x8*>(lds + (R * 8 + (c ^ ks(R))) * 8);
+    } else {
+        constexpr int CPR = ROWS / 8;
+        // ds_read_b64_tr_b16: within each 16-lane group, source lane 4s+q names k row s, columns
+        // 4q..4q+3 of a 4 x 16 block; result lane t receives column t of the four rows
+        const int g = lane >> 4, t = lane & 15, s = t >> 2, q = t & 3;
+        const int mn = mn_base + 16 * (g & 1) + 4 * q;
+        const int k = kk * 16 + 8 * (g >> 1) + s;
+        const int c = mn >> 3, half = (mn >> 2) & 1;
+        const uint16_t* p0 = lds + (k * CPR + (c ^ ms(k))) * 8 + half * 4;
+        const int k4 = k + 4;
+        const uint16_t* p1 = lds + (k4 * CPR + (c ^ ms(k4))) * 8 + half * 4;
+        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MB_LDS i16x4*)(p0));
+        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MB_LDS i16x4*)(p1));
+        i16x4 both[2] = {lo, hi};
+        bf16x8 out;
+        __builtin_memcpy(&out, both, 16);
+        return out;
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    // s_waitcnt with vmcnt = N (bits 3:0 and 15:14), expcnt and lgkmcnt left at their maxima (no wait)
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <bool P_KMAJOR, bool Q_KMAJOR, int EPI, class C>
+__global__ void __launch_bounds__(C::NT, 2) ns_gemm_fast(GemmArgs args) {
+    const int per_slot = (EPI == EPI_UPDATE) ? args.tiles_m * args.tiles_n : args.tiles_m * (args.tiles_m + 1) / 2;
+    const int total = args.batch * per_slot;
+    const int per_xcd = (total + 7) >> 3;
+    const int w = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+    if (w >= total) return;
+    const int slot = w / per_slot;
+    const int tile = w - slot * per_slot;
+    const bool live = args.live[slot] != 0;
+    if (!live && EPI != EPI_UPDATE) return;
+    int ti, tj;
+    if (EPI == EPI_UPDATE) {
+        ti = tile / args.tiles_n;
+        tj = tile % args.tiles_n;
+    } else {
+        sym_tile(tile, args.tiles_m, ti, tj);
+    }
+    const int i0 = ti * C::BM, j0 = tj * C::BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    uint16_t* out = args.out + (int64_t)slot * args.o_stride;
+
+    if (!live) {
+        for (int v = tid; v < C::BM * C::BN; v += C::NT) {
+            int i = i0 + v / C::BN, j = j0 + v % C::BN;
+            out[(int64_t)i * args.ldo + j] = 0;
+        }
+        return;
+    }
+
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * C::STAGE];
+    const i32x4 P = make_rsrc(args.P + (int64_t)slot * args.p_stride, (uint32_t)(args.p_stride * 2));
+    const i32x4 Q = make_rsrc(args.Q + (int64_t)slot * args.q_stride, (uint32_t)(args.q_stride * 2));
+    const int ldp = (int)args.ldp, ldq = (int)args.ldq;
+
+    f32x16 acc[C::FM][C::FN];
+#pragma unroll
+    for (int a = 0; a < C::FM; ++a)
+#pragma unroll
+        for (int b = 0; b < C::FN; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+
+    const int KT = args.K / BK;
+    load_tile_lds<P_KMAJOR, C::BM, C::NW>(P, ldp, i0, 0, smem, wave, lane);
+    load_tile_lds<Q_KMAJOR, C::BN, C::NW>(Q, ldq, j0, 0, smem + C::BM * 64, wave, lane);
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+
+    // fragments double-buffered in registers: the reads of step kk+1 are issued before
+    // the MFMAs of step kk, and the first reads of the next stage right after the barrier,
+    // ahead of the last MFMAs of the current one
+    bf16x8 pf[2][C::FM], qf[2][C::FN];
+#pragma unroll
+    for (int a = 0; a < C::FM; ++a) pf[0][a] = read_frag_fast<P_KMAJOR, C::BM>(smem, wm * C::TM + a * 32, 0, lane);
+#pragma unroll
+    for (int b = 0; b < C::FN; ++b)
+        qf[0][b] = read_frag_fast<Q_KMAJOR, C::BN>(smem + C::BM * 64, wn * C::TN + b * 32, 0, lane);
+
+    for (int kt = 0; kt < KT; ++kt) {
+        const int cur = kt & 1;
+        const uint16_t* lp = smem + cur * C::STAGE;
+        const bool more = kt + 1 < KT;
+        if (more) {
+            uint16_t* np = smem + (cur ^ 1) * C::STAGE;
+            load_tile_lds<P_KMAJOR, C::BM, C::NW>(P, ldp, i0, (kt + 1) * BK, np, wave, lane);
+            load_tile_lds<Q_KMAJOR, C::BN, C::NW>(Q, ldq, j0, (kt + 1) * BK, np + C::BM * 64, wave, lane);
+        }
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            const int fb = kk & 1, nb = fb ^ 1;
+            if (kk + 1 < BK / 16) {
+#pragma unroll
+                for (int a = 0; a < C::FM; ++a)
+                    pf[nb][a] = read_frag_fast<P_KMAJOR, C::BM>(lp, wm * C::TM + a * 32, kk + 1, lane);
+#pragma unroll
+                for (int b = 0; b < C::FN; ++b)
+                    qf[nb][b] = read_frag_fast<Q_KMAJOR, C::BN>(lp + C::BM * 64, wn * C::TN + b * 32, kk + 1, lane);
+            } else if (more) {
+                // every wave's reads of this stage are done and the next stage has landed
+                __builtin_amdgcn_s_waitcnt(0);
+                __builtin_amdgcn_s_barrier();
+                const uint16_t* np = smem + (cur ^ 1) * C::STAGE;
+#pragma unroll
+                for (int a = 0; a < C::FM; ++a)
+                    pf[nb][a] = read_frag_fast<P_KMAJOR, C::BM>(np, wm * C::TM + a * 32, 0, lane);
+#pragma unroll
+                for (int b = 0; b < C::FN; ++b)
+                    qf[nb][b] = read_frag_fast<Q_KMAJOR, C::BN>(np + C::BM * 64, wn * C::TN + b * 32, 0, lane);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int a = 0; a < C::FM; ++a)
+#pragma unroll
+                for (int b = 0; b < C::FN; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[fb][b], pf[fb][a], acc[a][b], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // ---- epilogue: lane holds C[i][j] for i = i_base + lane%32, j = j_base + 8g + 4*(lane/32) + 0..3
+    float sig = 1.f;
+    if (args.scale) {
+        const float s = args.scale[slot];
+        sig = (EPI == EPI_GRAM) ? s * s : s;
+    }
+    const uint16_t* aux = args.aux ? args.aux + (int64_t)slot * args.aux_stride : nullptr;
+    const bool mirror = (EPI != EPI_UPDATE) && (ti != tj);
+#pragma unroll
+    for (int a = 0; a < C::FM; ++a) {
+        const int i = i0 + wm * C::TM + a * 32 + (lane & 31);
+#pragma unroll
+        for (int b = 0; b < C::FN; ++b) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int jb = j0 + wn * C::TN + b * 32 + 8 * g + 4 * (lane >> 5);
+                float av[4] = {0.f, 0.f, 0.f, 0.f};
+                if (EPI != EPI_GRAM) {
+                    u32x2 wv = *reinterpret_cast<const u32x2*>(aux + (int64_t)i * args.ld_aux + jb);
+                    av[0] = __uint_as_float(wv[0] << 16);
+                    av[1] = __uint_as_float(wv[0] & 0xFFFF0000u);
+                    av[2] = __uint_as_float(wv[1] << 16);
+                    av[3] = __uint_as_float(wv[1] & 0xFFFF0000u);
+                }
+                uint16_t hb[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float x = acc[a][b][4 * g + r];
+                    float y;
+                    if (EPI == EPI_GRAM) y = sig * x;
+                    else if (EPI == EPI_POLY) y = __fmaf_rn(args.beta, av[r], args.alpha * x);
+                    else y = sig * __fmaf_rn(args.beta, av[r], x);
+                    hb[r] = f32_to_bf16_rne(y);
+                }
+                u32x2 wv;
+                wv[0] = (uint32_t)hb[0] | ((uint32_t)hb[1] << 16);
+                wv[1] = (uint32_t)hb[2] | ((uint32_t)hb[3] << 16);
+                *reinterpret_cast<u32x2*>(out + (int64_t)i * args.ldo + jb) = wv;
+                if (mirror) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) out[(int64_t)(jb + r) * args.ldo + i] = hb[r];
+                }
+            }
+        }
+    }
+}
+
+// Tile configuration of one contraction: 256x256 tiles move half the bytes per flop out of L2
+// but come in quarter the number; take them unless that leaves most of the chip idle.
+enum TileChoice { TILE_GENERIC = 0, TILE_128 = 1, TILE_256 = 2 };
+
+TileChoice pick_tile(int M, int N, int K, int batch, bool symmetric, bool transposed, bool vec) {
+    if (!vec || K % BK != 0) return TILE_GENERIC;
+    const bool fit256 = M % 256 == 0 && N % 256 == 0;
+    const bool fit128 = M % 128 == 0 && N % 128 == 0;
+    if (!fit128) return TILE_GENERIC;
+    if (!fit256) return TILE_128;
+    auto tiles = [&](int t) {
+        const int64_t tm = M / t, tn = N / t;
+        return (int64_t)batch * (symmetric ? tm * (tm + 1) / 2 : tm * tn);
+    };
+    // rounds of the whole grid over 256 CUs (128-tiles: two per CU) times the measured cost of
+    // one round: a round of 256-tiles (four times the work) takes about 1.4x a round of
+    // 128-tiles, 1.5x when an operand goes through the transposing LDS reads
+    const double r128 = std::ceil(tiles(128) / 512.0);
+    const double r256 = std::ceil(tiles(256) / 256.0) * (transposed ? 1.5 : 1.4);
+    return r256 <= r128 ? TILE_256 : TILE_128;
+}
+
 template <bool PK, bool QK, int EPI>
-hipError_t launch_gemm(const GemmArgs& a, int batch, bool vec, hipStream_t stream) {
-    const int tiles = (EPI == EPI_UPDATE) ? a.tiles_m * a.tiles_n : a.tiles_m * (a.tiles_m + 1) / 2;
-    dim3 grid((unsigned)tiles, (unsigned)batch);
-    if (vec) ns_gemm_kernel<PK, QK, EPI, true><<<grid, NT, 0, stream>>>(a);
+hipError_t launch_gemm(GemmArgs a, int batch, bool vec, hipStream_t stream) {
+    const bool sym = EPI != EPI_UPDATE;
+    const TileChoice tc = pick_tile(a.M, a.N, a.K, batch, sym, !(PK && QK), vec);
+    const int t = tc == TILE_256 ? 256 : 128;
+    a.tiles_m = (a.M + t - 1) / t;
+    a.tiles_n = (a.N + t - 1) / t;
+    a.batch = batch;
+    const int tiles = sym ? a.tiles_m * (a.tiles_m + 1) / 2 : a.tiles_m * a.tiles_n;
+    const int64_t total = (int64_t)tiles * batch;
+    dim3 grid((unsigned)(((total + 7) / 8) * 8));
+    if (tc == TILE_256) ns_gemm_fast<PK, QK, EPI, Cfg256><<<grid, Cfg256::NT, 0, stream>>>(a);
+    else if (tc == TILE_128) ns_gemm_fast<PK, QK, EPI, Cfg128><<<grid, Cfg128::NT, 0, stream>>>(a);
+    else if (vec) ns_gemm_kernel<PK, QK, EPI, true><<<grid, NT, 0, stream>>>(a);
     else ns_gemm_kernel<PK, QK, EPI, false><<<grid, NT, 0, stream>>>(a);
     return hipGetLastError();
 }
