@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--config", type=int, default=1, help="workload id 0..4 (1 = attention bank, the metric's case)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-parity", action="store_true")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run one device-to-device copy of MIB MiB (the known-size reference that the "
+                        "FETCH_SIZE / WRITE_SIZE counters of the kernels are scaled by) and exit")
     return p.parse_args()
 
 
@@ -63,6 +66,15 @@ def main():
     import torch
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU (HIP device)")
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n}), flush=True)
+        return
     sys.path.insert(0, HERE)
     from newton_schulz_bank_amd import api
     from newton_schulz_bank_amd.workloads import CONFIG_NAMES, CONFIGS, make_bank
