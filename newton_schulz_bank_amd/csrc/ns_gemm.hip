@@ -509,25 +509,53 @@ __global__ void __launch_bounds__(C::NT, 2) ns_gemm_fast(GemmArgs args) {
         }
     }
 
-    // ---- epilogue: lane holds C[i][j] for i = i_base + lane%32, j = j_base + 8g + 4*(lane/32) + 0..3
+    // ---- epilogue, staged through LDS so that every global access is a full coalesced row:
+    //   1. (polynomial, update) the aux tile A or X is copied into LDS with 16-byte loads;
+    //   2. each lane computes y for its accumulators (lane holds C[i][j..j+3] for
+    //      i = i_base + lane%32, j = j_base + 8g + 4*(lane/32)), reading aux from LDS and
+    //      writing y in place;
+    //   3. the tile is stored row by row with 16-byte stores;
+    //   4. off-diagonal symmetric tiles are re-staged transposed and stored the same way.
+    // Tile rows hold BN/8 16-byte chunks; chunk c of row i sits at chunk position c ^ (i % CW),
+    // so the 32 rows an accumulator access touches spread over the banks.
+    constexpr int CPRO = C::BN / 8;                     // 16-byte chunks per tile row
+    constexpr int CW = CPRO < 32 ? CPRO : 32;
+    static_assert(C::BM == C::BN || EPI == EPI_UPDATE, "symmetric tiles are square");
     float sig = 1.f;
     if (args.scale) {
         const float s = args.scale[slot];
         sig = (EPI == EPI_GRAM) ? s * s : s;
     }
-    const uint16_t* aux = args.aux ? args.aux + (int64_t)slot * args.aux_stride : nullptr;
     const bool mirror = (EPI != EPI_UPDATE) && (ti != tj);
+    uint16_t* st = smem;                                 // BM x BN bf16 staging tile (fits the ring)
+    auto spos = [&](int i, int c) { return i * C::BN + ((c ^ (i % CW)) << 3); };
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    if (EPI != EPI_GRAM) {
+        const uint16_t* aux = args.aux + (int64_t)slot * args.aux_stride;
+        constexpr int CH = C::BM * CPRO;
+#pragma unroll 4
+        for (int v = tid; v < CH; v += C::NT) {
+            const int i = v / CPRO, c = v % CPRO;
+            const u32x4 x = *reinterpret_cast<const u32x4*>(aux + (int64_t)(i0 + i) * args.ld_aux + j0 + c * 8);
+            *reinterpret_cast<u32x4*>(st + spos(i, c)) = x;
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
+    }
+    uint32_t yb[C::FM][C::FN][4][2];                     // y, packed bf16 pairs (kept for the transposed copy)
 #pragma unroll
     for (int a = 0; a < C::FM; ++a) {
-        const int i = i0 + wm * C::TM + a * 32 + (lane & 31);
+        const int i = wm * C::TM + a * 32 + (lane & 31);
 #pragma unroll
         for (int b = 0; b < C::FN; ++b) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int jb = j0 + wn * C::TN + b * 32 + 8 * g + 4 * (lane >> 5);
+                const int j = wn * C::TN + b * 32 + 8 * g + 4 * (lane >> 5);
+                uint16_t* p = st + spos(i, j >> 3) + (j & 4);
                 float av[4] = {0.f, 0.f, 0.f, 0.f};
                 if (EPI != EPI_GRAM) {
-                    u32x2 wv = *reinterpret_cast<const u32x2*>(aux + (int64_t)i * args.ld_aux + jb);
+                    const u32x2 wv = *reinterpret_cast<const u32x2*>(p);
                     av[0] = __uint_as_float(wv[0] << 16);
                     av[1] = __uint_as_float(wv[0] & 0xFFFF0000u);
                     av[2] = __uint_as_float(wv[1] << 16);
@@ -546,12 +574,49 @@ __global__ void __launch_bounds__(C::NT, 2) ns_gemm_fast(GemmArgs args) {
                 u32x2 wv;
                 wv[0] = (uint32_t)hb[0] | ((uint32_t)hb[1] << 16);
                 wv[1] = (uint32_t)hb[2] | ((uint32_t)hb[3] << 16);
-                *reinterpret_cast<u32x2*>(out + (int64_t)i * args.ldo + jb) = wv;
-                if (mirror) {
+                *reinterpret_cast<u32x2*>(p) = wv;
+                yb[a][b][g][0] = wv[0];
+                yb[a][b][g][1] = wv[1];
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    {
+        constexpr int CH = C::BM * CPRO;
+#pragma unroll 4
+        for (int v = tid; v < CH; v += C::NT) {
+            const int i = v / CPRO, c = v % CPRO;
+            *reinterpret_cast<u32x4*>(out + (int64_t)(i0 + i) * args.ldo + j0 + c * 8) =
+                *reinterpret_cast<const u32x4*>(st + spos(i, c));
+        }
+    }
+    if (mirror) {
+        // y^T: lane's y(i, j..j+3) goes to rows j..j+3, column i of the transposed tile
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) out[(int64_t)(jb + r) * args.ldo + i] = hb[r];
+        for (int a = 0; a < C::FM; ++a) {
+            const int i = wm * C::TM + a * 32 + (lane & 31);
+#pragma unroll
+            for (int b = 0; b < C::FN; ++b) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int j = wn * C::TN + b * 32 + 8 * g + 4 * (lane >> 5);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        st[spos(j + r, i >> 3) + (i & 7)] = (uint16_t)(yb[a][b][g][r >> 1] >> (16 * (r & 1)));
                 }
             }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
+        constexpr int CH = C::BM * CPRO;
+#pragma unroll 4
+        for (int v = tid; v < CH; v += C::NT) {
+            const int jr = v / CPRO, c = v % CPRO;
+            *reinterpret_cast<u32x4*>(out + (int64_t)(j0 + jr) * args.ldo + i0 + c * 8) =
+                *reinterpret_cast<const u32x4*>(st + spos(jr, c));
         }
     }
 }
