@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--config", type=int, default=1, help="workload id 0..4 (1 = attention bank, the metric's case)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-parity", action="store_true")
+    p.add_argument("--ns-path", type=int, default=0, choices=(0, 1),
+                   help="0: persistent Newton-Schulz kernel where the shape allows it; 1: one launch per contraction")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run one device-to-device copy of MIB MiB (the known-size reference that the "
                         "FETCH_SIZE / WRITE_SIZE counters of the kernels are scaled by) and exit")
@@ -80,6 +82,7 @@ def main():
     from newton_schulz_bank_amd.workloads import CONFIG_NAMES, CONFIGS, make_bank
 
     api.lib()    # fails loudly if libmuonbank.so is missing
+    api.mb_ns_set_path(args.ns_path)
     specs = CONFIGS[args.config]
     hosts = [make_bank(args.config, i) for i in range(len(specs))]
 
@@ -128,11 +131,16 @@ def main():
     api.mb_timing_enable(False)
 
     live_slots = sum(len(s.live_slots) for s in specs)
-    alg = {"ns_gram": 0, "ns_poly": 0, "ns_update": 0}
+    # algorithmic flops by the kernel that does them: banks whose sides are multiples of 256 run
+    # all their rounds in the persistent kernel (unless --ns-path 1), the rest one launch per
+    # contraction
+    alg = {"ns_persist": 0, "ns_gram": 0, "ns_poly": 0, "ns_update": 0}
     for s in specs:
         f = ns_flops_per_slot(s.rows, s.cols)
-        for k in alg:
-            alg[k] += f[k] * len(s.live_slots)
+        persistent = args.ns_path == 0 and s.rows % 256 == 0 and s.cols % 256 == 0
+        for k in ("ns_gram", "ns_poly", "ns_update"):
+            alg["ns_persist" if persistent else k] += f[k] * len(s.live_slots)
+    alg = {k: v for k, v in alg.items() if v > 0}
     ns_flops = sum(alg.values())
     bytes_ = {"momentum": sum(bank_bytes(s)["momentum"] for s in specs),
               "apply": sum(bank_bytes(s)["apply"] for s in specs)}
@@ -173,7 +181,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": CONFIG_NAMES[args.config], "config_id": args.config,
                    "banks": [[s.batch, s.rows, s.cols] for s in specs], "live_slots": live_slots,
-                   "ns_steps": 5, "grad_dtype": specs[0].grad_dtype},
+                   "ns_steps": 5, "grad_dtype": specs[0].grad_dtype, "ns_path": args.ns_path},
         "matrices_per_s": round(live_slots / (ms_per_step * 1e-3), 1),
         "ns_ms_per_step": round(ns_ms, 4),
         "ns_tflops": round(ns_flops / (ns_ms * 1e-3) / 1e12, 2) if ns_ms > 0 else None,
@@ -277,8 +285,11 @@ def read_traffic(kernel: str, config: int):
         if not entry:
             return None
         import hashlib
-        src = open(os.path.join(HERE, "newton_schulz_bank_amd", "csrc", entry["source"]), "rb").read()
-        if hashlib.sha256(src).hexdigest() != entry["source_sha256"]:
+        names = entry["sources"] if "sources" in entry else [entry["source"]]
+        h = hashlib.sha256()
+        for name in names:
+            h.update(open(os.path.join(HERE, "newton_schulz_bank_amd", "csrc", name), "rb").read())
+        if h.hexdigest() != entry["source_sha256"]:
             return None
         return entry["bytes_per_launch"]
     except Exception:

@@ -139,6 +139,18 @@ mb_status mp_apply_update(uint16_t *w_hi, uint16_t *w_lo, const uint16_t *v,
                           int64_t batch, int64_t slot_numel, float eff_lr, float decay,
                           const float *lr_mul_per_slot, void *stream);
 
+/* How stage 2 is scheduled (process-wide; the arithmetic is the same either way).
+ *   0 (default): when both sides of a slot are multiples of 256, every round of a
+ *     bank runs in one persistent launch: the 256x256 output tiles of all three
+ *     contractions of all rounds are tasks in per-XCD queues, and a task starts as
+ *     soon as the previous contraction of its own slot has finished.  Each slot's
+ *     tasks run on one XCD (slot s on XCD s % number of XCDs), so its intermediate
+ *     results stay coherent through that XCD's L2.
+ *   1: one launch per contraction and round.
+ * Returns the previous value, or -1 (nothing changed) for any other value.  Calls
+ * already enqueued are not affected. */
+int32_t mb_ns_set_path(int32_t path);
+
 /* Kernel timing (off by default).  While enabled, every kernel the library
  * launches is bracketed by two hipEvents on its stream; mb_timing_read waits
  * for them and returns, per kernel name, the launch count and the summed

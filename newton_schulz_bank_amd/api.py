@@ -56,7 +56,7 @@ _lib = None
 
 EXPORTED = ("mb_default_hparams", "mb_status_string", "mb_last_error", "mb_version", "mb_step_workspace_bytes",
             "mb_ns_workspace_bytes", "muon_bank_step", "muon_momentum_update", "ns_orthogonalize_batched",
-            "mp_apply_update", "mb_timing_enable", "mb_timing_read")
+            "mp_apply_update", "mb_ns_set_path", "mb_timing_enable", "mb_timing_read")
 
 
 def lib() -> ctypes.CDLL:
@@ -80,6 +80,7 @@ def lib() -> ctypes.CDLL:
         "muon_momentum_update": (i32, [vp, vp, vp, i64, i64, i64, i32, f32, f32, vp]),
         "ns_orthogonalize_batched": (i32, [vp, vp, i64, i64, i64, i32, f64, f64, f64, f64, vp, sz, vp]),
         "mp_apply_update": (i32, [vp, vp, vp, i64, i64, f32, f32, vp, vp]),
+        "mb_ns_set_path": (i32, [i32]),
         "mb_timing_enable": (None, [i32]),
         "mb_timing_read": (i32, [ctypes.POINTER(mb_kernel_time), i32]),
     }
@@ -255,6 +256,15 @@ def mp_apply_update(w_hi: torch.Tensor, w_lo: torch.Tensor, v: torch.Tensor, eff
         _dense(lr_mul_per_slot, "lr_mul_per_slot", 4)
     _check(lib().mp_apply_update(_ptr(w_hi), _ptr(w_lo), _ptr(v), batch, slot, float(eff_lr), float(decay),
                                  _ptr(lr_mul_per_slot), _stream(stream)))
+
+
+def mb_ns_set_path(path: int) -> int:
+    """0: persistent Newton-Schulz launch where the shape allows it; 1: one launch per contraction.
+    Returns the previous setting."""
+    prev = lib().mb_ns_set_path(int(path))
+    if prev < 0:
+        raise ValueError(f"unknown Newton-Schulz path {path}")
+    return prev
 
 
 def mb_timing_enable(on: bool) -> None:

@@ -13,6 +13,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 #define MB_LDS __attribute__((address_space(3)))
 
@@ -24,6 +26,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     uint32_t b = __float_as_uint(f);
     b += 0x7FFFu + ((b >> 16) & 1u);
     return (uint16_t)(b >> 16);
+}
+
+// Two floats -> packed bf16 bits (first in the low half), round to nearest even, with the
+// gfx950 conversion instruction (v_cvt_pk_bf16_f32).  Identical to f32_to_bf16_rne on every
+// finite input, denormals included, in the default (denormal-preserving) float mode.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_rne(float a, float b) {
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // Knuth's TwoSum: the exact error of s = RN(a + b), so that a + b = s + err.

@@ -24,9 +24,10 @@ hipError_t launch_momentum(const void* grad, void* buf, uint16_t* u, float* part
 // Per-(slot, chunk) sums of x^2 of a bf16 bank.
 hipError_t launch_sumsq(const uint16_t* x, float* partials, int64_t batch, int64_t slot_numel, bool vec,
                         hipStream_t stream);
-// scale[i] = 1 / (sqrt(sum of slot i's partials) + eps); live[i] = (sum > 0).
+// scale[i] = 1 / (sqrt(sum of slot i's partials) + eps); live[i] = (sum > 0).  If sync is
+// non-null, also clears the persistent kernel's queue heads, error word and slot counters.
 hipError_t launch_ns_scale(const float* partials, int nchunks, int64_t batch, float eps, float* scale, int* live,
-                           hipStream_t stream);
+                           int* sync, hipStream_t stream);
 // The mixed-precision apply on [batch, slot_numel].
 hipError_t launch_apply(uint16_t* w_hi, uint16_t* w_lo, const uint16_t* v, int64_t batch, int64_t slot_numel,
                         bool vec, float eta, float decay, const float* lr_mul_per_slot, hipStream_t stream);
@@ -44,5 +45,26 @@ struct NsRound {
     const int* live;
 };
 hipError_t ns_round(const NsRound& r, hipStream_t stream, RoundTimer* timer);
+
+// Every Newton-Schulz round of a bank in one persistent launch (x0 -> ... -> dest), with xa, xb
+// as ping-pong buffers, A and Bm as scratch and sync (ns_persist_sync_ints ints, cleared by
+// launch_ns_scale) for the task queues and per-slot counters.
+struct NsPersist {
+    const uint16_t* x0;
+    uint16_t* xa;
+    uint16_t* xb;
+    uint16_t* dest;
+    uint16_t* A;
+    uint16_t* Bm;
+    const float* scale;
+    const int* live;
+    int* sync;
+    int64_t batch, rows, cols;
+    int steps;
+    float a, b, c;
+};
+bool ns_persist_eligible(int64_t rows, int64_t cols, int steps);
+int ns_persist_sync_ints(int64_t batch);
+hipError_t ns_persist(const NsPersist& r, hipStream_t stream);
 
 }  // namespace mb

@@ -3,6 +3,7 @@
 // The operations are stated in include/muonbank.h.
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -161,9 +162,10 @@ mb_status check_hparams(const mb_hparams& hp) {
 
 size_t round_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Workspace of one bank: u, two ping-pong X buffers, A, B, partial sums, scale, live.
+// Workspace of one bank: u, two ping-pong X buffers, A, B, partial sums, scale, live, and the
+// persistent kernel's queue heads and slot counters (32 ints per slot group + one per slot).
 struct BankWs {
-    size_t u, x1, x2, A, Bm, partials, scale, live, total;
+    size_t u, x1, x2, A, Bm, partials, scale, live, sync, total;
 };
 
 BankWs bank_ws_layout(int64_t batch, int64_t rows, int64_t cols, bool vec) {
@@ -180,17 +182,31 @@ BankWs bank_ws_layout(int64_t batch, int64_t rows, int64_t cols, bool vec) {
     w.partials = off; off += round_up((size_t)batch * mb::stream_chunks(rows * cols, vec) * 4);
     w.scale = off; off += round_up((size_t)batch * 4);
     w.live = off; off += round_up((size_t)batch * 4);
+    w.sync = off; off += round_up((size_t)(32 * kLanes + batch) * 4);
     w.total = off;
     return w;
 }
 
 float f32(double v) { return (float)v; }
 
-// Newton-Schulz rounds on scaled input: x_first -> ... -> dest.  x1, x2 are
-// ping-pong buffers distinct from x_first and dest.
+// 0: every round of a bank in one persistent launch where the shape allows it; 1: one launch per
+// contraction.
+std::atomic<int> g_ns_path{0};
+
+// Newton-Schulz rounds on scaled input: x_first -> ... -> dest.  x1, x2 are ping-pong buffers
+// distinct from x_first and dest; sync (cleared by the ns_scale launch) serves the persistent
+// kernel.
 mb_status run_ns(const uint16_t* x_first, uint16_t* dest, uint16_t* x1, uint16_t* x2, uint16_t* A, uint16_t* Bm,
                  int64_t batch, int64_t rows, int64_t cols, int steps, double a, double b, double c,
-                 const float* scale, const int* live, hipStream_t stream, Timer& timer) {
+                 const float* scale, const int* live, int* sync, hipStream_t stream, Timer& timer) {
+    if (g_ns_path.load() == 0 && mb::ns_persist_eligible(rows, cols, steps)) {
+        mb::NsPersist r{x_first, x1, x2, dest, A, Bm, scale, live, sync, batch, rows, cols, steps, f32(a), f32(b), f32(c)};
+        timer.begin("ns_persist", stream);
+        hipError_t e = mb::ns_persist(r, stream);
+        timer.end(stream);
+        if (e != hipSuccess) return fail(MB_ERR_HIP, "Newton-Schulz launch: %s", hipGetErrorString(e));
+        return MB_OK;
+    }
     const uint16_t* in = x_first;
     for (int s = 0; s < steps; ++s) {
         const bool last = s == steps - 1;
@@ -320,13 +336,14 @@ mb_status ns_orthogonalize_batched(const uint16_t* x, uint16_t* y, int64_t batch
     timer.end(st);
     if (e != hipSuccess) return fail(MB_ERR_HIP, "sumsq launch: %s", hipGetErrorString(e));
     timer.begin("ns_scale", st);
-    e = mb::launch_ns_scale(partials, mb::stream_chunks(rows * cols, vec), batch, f32(eps), scale, live, st);
+    int* sync = (int*)(ws + L.sync);
+    e = mb::launch_ns_scale(partials, mb::stream_chunks(rows * cols, vec), batch, f32(eps), scale, live, sync, st);
     timer.end(st);
     if (e != hipSuccess) return fail(MB_ERR_HIP, "ns_scale launch: %s", hipGetErrorString(e));
     // in place with a single round: write the round to scratch, then copy
     uint16_t* dest = (x == y && steps == 1) ? (uint16_t*)(ws + L.u) : y;
     s = run_ns(x, dest, x1, x2, (uint16_t*)(ws + L.A), (uint16_t*)(ws + L.Bm), batch, rows, cols, steps, a, b, c,
-               scale, live, st, timer);
+               scale, live, sync, st, timer);
     if (s != MB_OK) return s;
     if (dest != y) {
         e = hipMemcpyAsync(y, dest, n * 2, hipMemcpyDeviceToDevice, st);
@@ -411,6 +428,7 @@ mb_status muon_bank_step(const mb_bank* banks, int32_t num_banks, const mb_hpara
     struct Unit {
         int32_t bank;
         int64_t s0, s1;
+        int32_t group;
     };
     std::vector<Unit> units;
     for (int32_t i = 0; i < num_banks; ++i) {
@@ -418,7 +436,7 @@ mb_status muon_bank_step(const mb_bank* banks, int32_t num_banks, const mb_hpara
         const bool big = b.rows * b.cols >= 65536 && b.batch >= 2 * kLanes;
         const int64_t groups = big ? kLanes : 1;
         for (int64_t g = 0; g < groups; ++g)
-            units.push_back({i, b.batch * g / groups, b.batch * (g + 1) / groups});
+            units.push_back({i, b.batch * g / groups, b.batch * (g + 1) / groups, (int32_t)g});
     }
     std::lock_guard<std::mutex> lk(g_streams_mu);
     DeviceStreams* ds = nullptr;
@@ -473,18 +491,20 @@ mb_status muon_bank_step(const mb_bank* banks, int32_t num_banks, const mb_hpara
         float* partials = (float*)(bw + L.partials) + s0 * nch;
         float* scale = (float*)(bw + L.scale) + s0;
         int* live = (int*)(bw + L.live) + s0;
+        int* sync = (int*)(bw + L.sync) + 32 * un.group + s0;
 
         timer.begin("momentum", us);
         hipError_t e = mb::launch_momentum(grad, mom, u, partials, nb, slot, b.grad_dtype == MB_F32, vec, mu, nu, us);
         timer.end(us);
         if (e != hipSuccess) return fail(MB_ERR_HIP, "momentum launch: %s", hipGetErrorString(e));
         timer.begin("ns_scale", us);
-        e = mb::launch_ns_scale(partials, nch, nb, f32(hp.eps), scale, live, us);
+        e = mb::launch_ns_scale(partials, nch, nb, f32(hp.eps), scale, live, sync, us);
         timer.end(us);
         if (e != hipSuccess) return fail(MB_ERR_HIP, "ns_scale launch: %s", hipGetErrorString(e));
         // with one round and no v_out, the round would read u while writing v in the same buffer
         uint16_t* dest = (hp.ns_steps == 1 && v == u) ? x2 : v;
-        s = run_ns(u, dest, x1, x2, A, Bm, nb, b.rows, b.cols, hp.ns_steps, hp.a, hp.b, hp.c, scale, live, us, timer);
+        s = run_ns(u, dest, x1, x2, A, Bm, nb, b.rows, b.cols, hp.ns_steps, hp.a, hp.b, hp.c, scale, live, sync, us,
+                   timer);
         if (s != MB_OK) return s;
         timer.begin("apply", us);
         e = mb::launch_apply(w_hi, w_lo, dest, nb, slot, vec, eta, decay, lrm, us);
@@ -503,6 +523,11 @@ mb_status muon_bank_step(const mb_bank* banks, int32_t num_banks, const mb_hpara
         }
     }
     return ok();
+}
+
+int32_t mb_ns_set_path(int32_t path) {
+    if (path != 0 && path != 1) return -1;
+    return g_ns_path.exchange(path);
 }
 
 void mb_timing_enable(int32_t on) {

@@ -29,6 +29,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "ns_tile.hpp"
 
 namespace mb {
 
@@ -55,8 +56,6 @@ struct GemmArgs {
     const float* scale;         // per-slot Frobenius scale (first round only), else null
     const int* live;            // per-slot live flag
 };
-
-enum { EPI_GRAM = 0, EPI_POLY = 1, EPI_UPDATE = 2 };
 
 // Registers staging one 128 (mn) x 64 (k) operand tile: four 16-byte vectors per thread.
 template <bool KMAJOR, bool VEC>
@@ -129,13 +128,6 @@ __device__ __forceinline__ bf16x8 read_frag(const uint16_t* lds, int mn_base, in
         __builtin_memcpy(&out, both, 16);
         return out;
     }
-}
-
-__device__ __forceinline__ void sym_tile(int t, int T, int& I, int& J) {
-    int i = 0;
-    while (t >= T - i) { t -= T - i; ++i; }
-    I = i;
-    J = i + t;
 }
 
 template <bool P_KMAJOR, bool Q_KMAJOR, int EPI, bool VEC>
@@ -299,112 +291,11 @@ __global__ void __launch_bounds__(NT, 2) ns_gemm_kernel(GemmArgs args) {
 
 // ---------------------------------------------------------------------------
 // Fast path for M, N multiples of the tile and K a multiple of 64 (every bank
-// shape).  Operand tiles are copied global -> LDS directly with MUBUF
-// buffer_load ... lds (16 B per lane) into a two-stage ring, so the copy of
-// stage k+1 overlaps the MFMAs of stage k with no register staging.  The LDS
-// layouts are XOR-swizzled so the 16-byte fragment reads and the transposing
-// reads hit distinct banks.  Tile shapes are template parameters: 128x128 with
-// four wavefronts (two workgroups per CU) or 256x256 with eight (one per CU,
-// twice the flops per byte moved out of L2).
+// shape): one workgroup per output tile, the tile body shared with the
+// persistent kernel.  Tile shapes: 128x128 with four wavefronts (two
+// workgroups per CU) or 256x256 with eight (one per CU, twice the flops per
+// byte moved out of L2).
 // ---------------------------------------------------------------------------
-
-// K-major tile [rows][8 chunks of 8 k]: chunk c of row R sits at entry R*8 + (c ^ ks(R)),
-// conflict-free for the 16 lanes a 16-byte read serves per cycle.
-__device__ __forceinline__ int ks(int R) { return (R & 7) ^ ((R >> 3) & 1); }
-// MN-major tile [64 k rows][rows/8 chunks of 8 mn]: chunk c of row k sits at entry
-// k*(rows/8) + (c ^ ms(k)).  A transposing read serves 32 lanes per cycle (4 k rows x 4
-// chunks x 2 halves), which the XOR with 4*(k & 3) spreads over all 64 banks.
-__device__ __forceinline__ int ms(int k) { return 4 * (k & 3); }
-
-// MUBUF load of 16 bytes per lane straight into LDS (lane l -> LDS base + 16*l).  Unlike the
-// FLAT-encoded global_load_lds it is tracked by vmcnt alone, so waiting for LDS reads never
-// waits for copies still in flight; reads past the descriptor's size return zeros.
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-extern "C" __device__ void mb_raw_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) uint32_t* lds,
-                                                  int size, int voffset, int soffset, int offset, int aux)
-    __asm("llvm.amdgcn.raw.buffer.load.lds");
-
-// Buffer descriptor of `bytes` bytes at `base` (raw buffer, stride 0; word 3 as for every gfx9 part).
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
-    const uint64_t a = (uint64_t)base;
-    i32x4 r;
-    r[0] = (int32_t)(uint32_t)a;
-    r[1] = (int32_t)(uint32_t)((a >> 32) & 0xFFFFu);
-    r[2] = (int32_t)bytes;
-    r[3] = 0x00020000;
-    return r;
-}
-
-template <int BM_, int BN_, int WM_, int WN_>
-struct Cfg {
-    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-    static constexpr int NW = WM * WN, NT = 64 * NW;
-    static constexpr int TM = BM / WM, TN = BN / WN;      // outputs per wavefront
-    static constexpr int FM = TM / 32, FN = TN / 32;      // 32x32 MFMA blocks per wavefront
-    static constexpr int STAGE = (BM + BN) * 64;          // elements per ring stage
-    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tiles are whole MFMA blocks");
-    static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "copy instructions split evenly");
-};
-using Cfg128 = Cfg<128, 128, 2, 2>;
-using Cfg256 = Cfg<256, 256, 2, 4>;
-
-// Copy one ROWS (mn) x 64 (k) operand tile into LDS: ROWS/8 instructions of 64 lanes x 16 B,
-// instruction q filling entries [64q, 64q + 64).
-template <bool KMAJOR, int ROWS, int NW>
-__device__ __forceinline__ void load_tile_lds(i32x4 rsrc, int ld, int mn0, int k0, uint16_t* lds, int wave,
-                                              int lane) {
-    constexpr int NI = ROWS / 8 / NW;
-    constexpr int CPR = ROWS / 8;                         // chunks per k row (MN-major)
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-        const int q = wave * NI + j;
-        int elem;
-        if (KMAJOR) {
-            const int R = q * 8 + (lane >> 3);
-            const int c = (lane & 7) ^ ks(R);
-            elem = (mn0 + R) * ld + k0 + c * 8;
-        } else {
-            const int k = q * (64 / CPR) + lane / CPR;
-            const int c = (lane % CPR) ^ ms(k);
-            elem = (k0 + k) * ld + mn0 + c * 8;
-        }
-        mb_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) uint32_t*)(lds + q * 512), 16, elem * 2, 0, 0,
-                               0);
-    }
-}
-
-// MFMA fragment (32 rows x 16 k; lane l holds row l%32, k = kk*16 + 8*(l/32) + 0..7) from a swizzled tile.
-template <bool KMAJOR, int ROWS>
-__device__ __forceinline__ bf16x8 read_frag_fast(const uint16_t* lds, int mn_base, int kk, int lane) {
-    if (KMAJOR) {
-        const int R = mn_base + (lane & 31);
-        const int c = 2 * kk + (lane >> 5);
-        return *reinterpret_cast<const bf16x8*>(lds + (R * 8 + (c ^ ks(R))) * 8);
-    } else {
-        constexpr int CPR = ROWS / 8;
-        // ds_read_b64_tr_b16: within each 16-lane group, source lane 4s+q names k row s, columns
-        // 4q..4q+3 of a 4 x 16 block; result lane t receives column t of the four rows
-        const int g = lane >> 4, t = lane & 15, s = t >> 2, q = t & 3;
-        const int mn = mn_base + 16 * (g & 1) + 4 * q;
-        const int k = kk * 16 + 8 * (g >> 1) + s;
-        const int c = mn >> 3, half = (mn >> 2) & 1;
-        const uint16_t* p0 = lds + (k * CPR + (c ^ ms(k))) * 8 + half * 4;
-        const int k4 = k + 4;
-        const uint16_t* p1 = lds + (k4 * CPR + (c ^ ms(k4))) * 8 + half * 4;
-        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MB_LDS i16x4*)(p0));
-        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MB_LDS i16x4*)(p1));
-        i16x4 both[2] = {lo, hi};
-        bf16x8 out;
-        __builtin_memcpy(&out, both, 16);
-        return out;
-    }
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    // s_waitcnt with vmcnt = N (bits 3:0 and 15:14), expcnt and lgkmcnt left at their maxima (no wait)
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 template <bool P_KMAJOR, bool Q_KMAJOR, int EPI, class C>
 __global__ void __launch_bounds__(C::NT, 2) ns_gemm_fast(GemmArgs args) {
@@ -425,200 +316,40 @@ __global__ void __launch_bounds__(C::NT, 2) ns_gemm_fast(GemmArgs args) {
         sym_tile(tile, args.tiles_m, ti, tj);
     }
     const int i0 = ti * C::BM, j0 = tj * C::BN;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave / C::WN, wn = wave % C::WN;
     uint16_t* out = args.out + (int64_t)slot * args.o_stride;
 
     if (!live) {
-        for (int v = tid; v < C::BM * C::BN; v += C::NT) {
+        for (int v = threadIdx.x; v < C::BM * C::BN; v += C::NT) {
             int i = i0 + v / C::BN, j = j0 + v % C::BN;
             out[(int64_t)i * args.ldo + j] = 0;
         }
         return;
     }
 
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * C::STAGE];
-    const i32x4 P = make_rsrc(args.P + (int64_t)slot * args.p_stride, (uint32_t)(args.p_stride * 2));
-    const i32x4 Q = make_rsrc(args.Q + (int64_t)slot * args.q_stride, (uint32_t)(args.q_stride * 2));
-    const int ldp = (int)args.ldp, ldq = (int)args.ldq;
-
-    f32x16 acc[C::FM][C::FN];
-#pragma unroll
-    for (int a = 0; a < C::FM; ++a)
-#pragma unroll
-        for (int b = 0; b < C::FN; ++b)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
-
-    const int KT = args.K / BK;
-    load_tile_lds<P_KMAJOR, C::BM, C::NW>(P, ldp, i0, 0, smem, wave, lane);
-    load_tile_lds<Q_KMAJOR, C::BN, C::NW>(Q, ldq, j0, 0, smem + C::BM * 64, wave, lane);
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-
-    // fragments double-buffered in registers: the reads of step kk+1 are issued before
-    // the MFMAs of step kk, and the first reads of the next stage right after the barrier,
-    // ahead of the last MFMAs of the current one
-    bf16x8 pf[2][C::FM], qf[2][C::FN];
-#pragma unroll
-    for (int a = 0; a < C::FM; ++a) pf[0][a] = read_frag_fast<P_KMAJOR, C::BM>(smem, wm * C::TM + a * 32, 0, lane);
-#pragma unroll
-    for (int b = 0; b < C::FN; ++b)
-        qf[0][b] = read_frag_fast<Q_KMAJOR, C::BN>(smem + C::BM * 64, wn * C::TN + b * 32, 0, lane);
-
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        const uint16_t* lp = smem + cur * C::STAGE;
-        const bool more = kt + 1 < KT;
-        if (more) {
-            uint16_t* np = smem + (cur ^ 1) * C::STAGE;
-            load_tile_lds<P_KMAJOR, C::BM, C::NW>(P, ldp, i0, (kt + 1) * BK, np, wave, lane);
-            load_tile_lds<Q_KMAJOR, C::BN, C::NW>(Q, ldq, j0, (kt + 1) * BK, np + C::BM * 64, wave, lane);
-        }
-#pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int fb = kk & 1, nb = fb ^ 1;
-            if (kk + 1 < BK / 16) {
-#pragma unroll
-                for (int a = 0; a < C::FM; ++a)
-                    pf[nb][a] = read_frag_fast<P_KMAJOR, C::BM>(lp, wm * C::TM + a * 32, kk + 1, lane);
-#pragma unroll
-                for (int b = 0; b < C::FN; ++b)
-                    qf[nb][b] = read_frag_fast<Q_KMAJOR, C::BN>(lp + C::BM * 64, wn * C::TN + b * 32, kk + 1, lane);
-            } else if (more) {
-                // every wave's reads of this stage are done and the next stage has landed
-                __builtin_amdgcn_s_waitcnt(0);
-                __builtin_amdgcn_s_barrier();
-                const uint16_t* np = smem + (cur ^ 1) * C::STAGE;
-#pragma unroll
-                for (int a = 0; a < C::FM; ++a)
-                    pf[nb][a] = read_frag_fast<P_KMAJOR, C::BM>(np, wm * C::TM + a * 32, 0, lane);
-#pragma unroll
-                for (int b = 0; b < C::FN; ++b)
-                    qf[nb][b] = read_frag_fast<Q_KMAJOR, C::BN>(np + C::BM * 64, wn * C::TN + b * 32, 0, lane);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int a = 0; a < C::FM; ++a)
-#pragma unroll
-                for (int b = 0; b < C::FN; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[fb][b], pf[fb][a], acc[a][b], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-
-    // ---- epilogue, staged through LDS so that every global access is a full coalesced row:
-    //   1. (polynomial, update) the aux tile A or X is copied into LDS with 16-byte loads;
-    //   2. each lane computes y for its accumulators (lane holds C[i][j..j+3] for
-    //      i = i_base + lane%32, j = j_base + 8g + 4*(lane/32)), reading aux from LDS and
-    //      writing y in place;
-    //   3. the tile is stored row by row with 16-byte stores;
-    //   4. off-diagonal symmetric tiles are re-staged transposed and stored the same way.
-    // Tile rows hold BN/8 16-byte chunks; chunk c of row i sits at chunk position c ^ (i % CW),
-    // so the 32 rows an accumulator access touches spread over the banks.
-    constexpr int CPRO = C::BN / 8;                     // 16-byte chunks per tile row
-    constexpr int CW = CPRO < 32 ? CPRO : 32;
-    static_assert(C::BM == C::BN || EPI == EPI_UPDATE, "symmetric tiles are square");
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[C::RING];
+    TileJob jb;
+    jb.P = make_rsrc(args.P + (int64_t)slot * args.p_stride, (uint32_t)(args.p_stride * 2));
+    jb.Q = make_rsrc(args.Q + (int64_t)slot * args.q_stride, (uint32_t)(args.q_stride * 2));
+    jb.X = EPI == EPI_GRAM ? jb.P
+                           : make_rsrc(args.aux + (int64_t)slot * args.aux_stride, (uint32_t)(args.aux_stride * 2));
+    jb.ldp = (int)args.ldp;
+    jb.ldq = (int)args.ldq;
+    jb.ldx = (int)args.ld_aux;
+    jb.ldo = (int)args.ldo;
+    jb.K = args.K;
+    jb.i0 = i0;
+    jb.j0 = j0;
+    jb.out = out;
+    jb.mirror = (EPI != EPI_UPDATE) && (ti != tj);
+    jb.alpha = args.alpha;
+    jb.beta = args.beta;
     float sig = 1.f;
     if (args.scale) {
         const float s = args.scale[slot];
         sig = (EPI == EPI_GRAM) ? s * s : s;
     }
-    const bool mirror = (EPI != EPI_UPDATE) && (ti != tj);
-    uint16_t* st = smem;                                 // BM x BN bf16 staging tile (fits the ring)
-    auto spos = [&](int i, int c) { return i * C::BN + ((c ^ (i % CW)) << 3); };
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_s_barrier();
-    if (EPI != EPI_GRAM) {
-        const uint16_t* aux = args.aux + (int64_t)slot * args.aux_stride;
-        constexpr int CH = C::BM * CPRO;
-#pragma unroll 4
-        for (int v = tid; v < CH; v += C::NT) {
-            const int i = v / CPRO, c = v % CPRO;
-            const u32x4 x = *reinterpret_cast<const u32x4*>(aux + (int64_t)(i0 + i) * args.ld_aux + j0 + c * 8);
-            *reinterpret_cast<u32x4*>(st + spos(i, c)) = x;
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        __builtin_amdgcn_s_barrier();
-    }
-    uint32_t yb[C::FM][C::FN][4][2];                     // y, packed bf16 pairs (kept for the transposed copy)
-#pragma unroll
-    for (int a = 0; a < C::FM; ++a) {
-        const int i = wm * C::TM + a * 32 + (lane & 31);
-#pragma unroll
-        for (int b = 0; b < C::FN; ++b) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int j = wn * C::TN + b * 32 + 8 * g + 4 * (lane >> 5);
-                uint16_t* p = st + spos(i, j >> 3) + (j & 4);
-                float av[4] = {0.f, 0.f, 0.f, 0.f};
-                if (EPI != EPI_GRAM) {
-                    const u32x2 wv = *reinterpret_cast<const u32x2*>(p);
-                    av[0] = __uint_as_float(wv[0] << 16);
-                    av[1] = __uint_as_float(wv[0] & 0xFFFF0000u);
-                    av[2] = __uint_as_float(wv[1] << 16);
-                    av[3] = __uint_as_float(wv[1] & 0xFFFF0000u);
-                }
-                uint16_t hb[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float x = acc[a][b][4 * g + r];
-                    float y;
-                    if (EPI == EPI_GRAM) y = sig * x;
-                    else if (EPI == EPI_POLY) y = __fmaf_rn(args.beta, av[r], args.alpha * x);
-                    else y = sig * __fmaf_rn(args.beta, av[r], x);
-                    hb[r] = f32_to_bf16_rne(y);
-                }
-                u32x2 wv;
-                wv[0] = (uint32_t)hb[0] | ((uint32_t)hb[1] << 16);
-                wv[1] = (uint32_t)hb[2] | ((uint32_t)hb[3] << 16);
-                *reinterpret_cast<u32x2*>(p) = wv;
-                yb[a][b][g][0] = wv[0];
-                yb[a][b][g][1] = wv[1];
-            }
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_s_barrier();
-    {
-        constexpr int CH = C::BM * CPRO;
-#pragma unroll 4
-        for (int v = tid; v < CH; v += C::NT) {
-            const int i = v / CPRO, c = v % CPRO;
-            *reinterpret_cast<u32x4*>(out + (int64_t)(i0 + i) * args.ldo + j0 + c * 8) =
-                *reinterpret_cast<const u32x4*>(st + spos(i, c));
-        }
-    }
-    if (mirror) {
-        // y^T: lane's y(i, j..j+3) goes to rows j..j+3, column i of the transposed tile
-        __builtin_amdgcn_s_waitcnt(0);
-        __builtin_amdgcn_s_barrier();
-#pragma unroll
-        for (int a = 0; a < C::FM; ++a) {
-            const int i = wm * C::TM + a * 32 + (lane & 31);
-#pragma unroll
-            for (int b = 0; b < C::FN; ++b) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int j = wn * C::TN + b * 32 + 8 * g + 4 * (lane >> 5);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        st[spos(j + r, i >> 3) + (i & 7)] = (uint16_t)(yb[a][b][g][r >> 1] >> (16 * (r & 1)));
-                }
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        __builtin_amdgcn_s_barrier();
-        constexpr int CH = C::BM * CPRO;
-#pragma unroll 4
-        for (int v = tid; v < CH; v += C::NT) {
-            const int jr = v / CPRO, c = v % CPRO;
-            *reinterpret_cast<u32x4*>(out + (int64_t)(j0 + jr) * args.ldo + i0 + c * 8) =
-                *reinterpret_cast<const u32x4*>(st + spos(jr, c));
-        }
-    }
+    jb.sig = sig;
+    gemm_tile<P_KMAJOR, Q_KMAJOR, EPI, C, POL_DEFAULT>(jb, smem, (int)threadIdx.x);
 }
 
 // Tile configuration of one contraction: 256x256 tiles move half the bytes per flop out of L2

@@ -1,0 +1,331 @@
+// One output tile of a Newton-Schulz contraction on gfx950, shared by the
+// per-phase kernels and the persistent dataflow kernel.
+//
+// A tile computes C[i][j] = sum_k P(i,k) Q(k,j) for one slot, with each operand
+// stored either K-major (row i holds P(i, 0..K)) or MN-major (row k holds
+// P(0..M, k)), then applies one of three fp32 epilogues and rounds once to bf16
+// (round to nearest even):
+//   GRAM   out = sig*acc              symmetric, mirrored
+//   POLY   out = alpha*acc + beta*A   symmetric, mirrored
+//   UPDATE out = sig*(acc + beta*X)
+// Operand tiles are copied global -> LDS with MUBUF buffer_load ... lds (16 B
+// per lane) into a two-stage ring, so the copy of stage k+1 overlaps the MFMAs
+// of stage k with no register staging.  (A ring of four 32-k slots, three in
+// flight, measured slower: twice the barriers and half-line row segments cost
+// more than the deeper prefetch gains.)  The LDS layouts are XOR-swizzled so the
+// 16-byte fragment reads and the transposing reads (ds_read_b64_tr_b16) hit
+// distinct banks.  Every global load takes a cache policy: 0, or sc1 so that a
+// load misses the CU's L1 and reads the XCD's L2, which is what a consumer of
+// data written during the same kernel by another CU of the same XCD needs.
+#pragma once
+
+#include "common.hpp"
+
+namespace mb {
+
+constexpr int kBK = 64;                 // k per ring stage
+enum { EPI_GRAM = 0, EPI_POLY = 1, EPI_UPDATE = 2 };
+enum { POL_DEFAULT = 0, POL_SC1 = 16 }; // cache-policy bits of MUBUF loads (bit 4 = sc1 on gfx940+)
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int NW = WM * WN, NT = 64 * NW;
+    static constexpr int TM = BM / WM, TN = BN / WN;      // outputs per wavefront
+    static constexpr int FM = TM / 32, FN = TN / 32;      // 32x32 MFMA blocks per wavefront
+    static constexpr int STAGE = (BM + BN) * kBK;         // elements per ring stage (P rows, then Q rows)
+    static constexpr int RING = 2 * STAGE;                // elements of the whole ring
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tiles are whole MFMA blocks");
+    static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "copy instructions split evenly");
+    static_assert(BM * BN <= RING, "the epilogue staging tile fits the ring");
+};
+using Cfg128 = Cfg<128, 128, 2, 2>;
+using Cfg256 = Cfg<256, 256, 2, 4>;
+
+// K-major tile [rows][8 chunks of 8 k]: chunk c of row R sits at entry R*8 + (c ^ ks(R)),
+// conflict-free for the 16 lanes a 16-byte read serves per cycle.
+__device__ __forceinline__ int ks(int R) { return (R & 7) ^ ((R >> 3) & 1); }
+// MN-major tile [64 k rows][rows/8 chunks of 8 mn]: chunk c of row k sits at entry
+// k*(rows/8) + (c ^ ms(k)).  A transposing read serves 32 lanes per cycle (4 k rows x 4
+// chunks x 2 halves), which the XOR with 4*(k & 3) spreads over all 64 banks.
+__device__ __forceinline__ int ms(int k) { return 4 * (k & 3); }
+
+// MUBUF load of 16 bytes per lane straight into LDS (lane l -> LDS base + 16*l).  Unlike the
+// FLAT-encoded global_load_lds it is tracked by vmcnt alone, so waiting for LDS reads never
+// waits for copies still in flight; reads past the descriptor's size return zeros.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+extern "C" __device__ void mb_raw_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) uint32_t* lds,
+                                                  int size, int voffset, int soffset, int offset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// Buffer descriptor of `bytes` bytes at `base` (raw buffer, stride 0; word 3 as for every gfx9 part).
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    i32x4 r;
+    r[0] = (int32_t)(uint32_t)a;
+    r[1] = (int32_t)(uint32_t)((a >> 32) & 0xFFFFu);
+    r[2] = (int32_t)bytes;
+    r[3] = 0x00020000;
+    return r;
+}
+
+// Copy one ROWS (mn) x 64 (k) operand tile into LDS: ROWS/8 instructions of 64 lanes x 16 B,
+// instruction q filling entries [64q, 64q + 64).
+template <bool KMAJOR, int ROWS, int NW, int POL>
+__device__ __forceinline__ void load_tile_lds(i32x4 rsrc, int ld, int mn0, int k0, uint16_t* lds, int wave,
+                                              int lane) {
+    constexpr int NI = ROWS / 8 / NW;
+    constexpr int CPR = ROWS / 8;                         // chunks per k row (MN-major)
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+        const int q = wave * NI + j;
+        int elem;
+        if (KMAJOR) {
+            const int R = q * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ ks(R);
+            elem = (mn0 + R) * ld + k0 + c * 8;
+        } else {
+            const int k = q * (64 / CPR) + lane / CPR;
+            const int c = (lane % CPR) ^ ms(k);
+            elem = (k0 + k) * ld + mn0 + c * 8;
+        }
+        mb_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) uint32_t*)(lds + q * 512), 16, elem * 2, 0, 0,
+                               POL);
+    }
+}
+
+// MFMA fragment (32 rows x 16 k; lane l holds row l%32, k = kk*16 + 8*(l/32) + 0..7) from a swizzled tile.
+template <bool KMAJOR, int ROWS>
+__device__ __forceinline__ bf16x8 read_frag_fast(const uint16_t* lds, int mn_base, int kk, int lane) {
+    if (KMAJOR) {
+        const int R = mn_base + (lane & 31);
+        const int c = 2 * kk + (lane >> 5);
+        return *reinterpret_cast<const bf16x8*>(lds + (R * 8 + (c ^ ks(R))) * 8);
+    } else {
+        constexpr int CPR = ROWS / 8;
+        // ds_read_b64_tr_b16: within each 16-lane group, source lane 4s+q names k row s, columns
+        // 4q..4q+3 of a 4 x 16 block; result lane t receives column t of the four rows
+        const int g = lane >> 4, t = lane & 15, s = t >> 2, q = t & 3;
+        const int mn = mn_base + 16 * (g & 1) + 4 * q;
+        const int k = kk * 16 + 8 * (g >> 1) + s;
+        const int c = mn >> 3, half = (mn >> 2) & 1;
+        const uint16_t* p0 = lds + (k * CPR + (c ^ ms(k))) * 8 + half * 4;
+        const int k4 = k + 4;
+        const uint16_t* p1 = lds + (k4 * CPR + (c ^ ms(k4))) * 8 + half * 4;
+        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MB_LDS i16x4*)(p0));
+        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MB_LDS i16x4*)(p1));
+        i16x4 both[2] = {lo, hi};
+        bf16x8 out;
+        __builtin_memcpy(&out, both, 16);
+        return out;
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    // s_waitcnt with vmcnt = N (bits 3:0 and 15:14), expcnt and lgkmcnt left at their maxima (no wait)
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Upper-triangle tile t (row-major over the triangle of a T x T tile grid) -> (I, J), I <= J.
+__device__ __forceinline__ void sym_tile(int t, int T, int& I, int& J) {
+    int i = 0;
+    while (t >= T - i) { t -= T - i; ++i; }
+    I = i;
+    J = i + t;
+}
+
+// What one tile needs: buffer descriptors of the slot's operands and aux, leading dimensions
+// (elements), the contraction length, the tile origin, and the epilogue scalars.
+struct TileJob {
+    i32x4 P, Q, X;          // operand P, operand Q, aux (A for POLY, X for UPDATE; unused for GRAM)
+    int ldp, ldq, ldx, ldo;
+    int K;                  // multiple of 64
+    int i0, j0;
+    uint16_t* out;          // the slot's output
+    bool mirror;            // also write the transposed tile (off-diagonal symmetric tiles)
+    float alpha, beta, sig;
+};
+
+// tid is the thread's index in the workgroup.  A caller that runs tiles in a loop passes it
+// through an opaque copy made inside the loop, so the per-lane address arithmetic is recomputed
+// per tile instead of being hoisted out of the loop and held in registers across it.
+template <bool P_KMAJOR, bool Q_KMAJOR, int EPI, class C, int POL>
+__device__ __forceinline__ void gemm_tile(const TileJob& jb, uint16_t* smem, int tid) {
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int i0 = jb.i0, j0 = jb.j0;
+
+    f32x16 acc[C::FM][C::FN];
+#pragma unroll
+    for (int a = 0; a < C::FM; ++a)
+#pragma unroll
+        for (int b = 0; b < C::FN; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+
+    const int KT = jb.K / kBK;
+    load_tile_lds<P_KMAJOR, C::BM, C::NW, POL>(jb.P, jb.ldp, i0, 0, smem, wave, lane);
+    load_tile_lds<Q_KMAJOR, C::BN, C::NW, POL>(jb.Q, jb.ldq, j0, 0, smem + C::BM * kBK, wave, lane);
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+
+    // fragments double-buffered in registers: the reads of step kk+1 are issued before
+    // the MFMAs of step kk, and the first reads of the next stage right after the barrier,
+    // ahead of the last MFMAs of the current one
+    bf16x8 pf[2][C::FM], qf[2][C::FN];
+#pragma unroll
+    for (int a = 0; a < C::FM; ++a) pf[0][a] = read_frag_fast<P_KMAJOR, C::BM>(smem, wm * C::TM + a * 32, 0, lane);
+#pragma unroll
+    for (int b = 0; b < C::FN; ++b)
+        qf[0][b] = read_frag_fast<Q_KMAJOR, C::BN>(smem + C::BM * kBK, wn * C::TN + b * 32, 0, lane);
+
+    for (int kt = 0; kt < KT; ++kt) {
+        const int cur = kt & 1;
+        const uint16_t* lp = smem + cur * C::STAGE;
+        const bool more = kt + 1 < KT;
+        if (more) {
+            uint16_t* np = smem + (cur ^ 1) * C::STAGE;
+            load_tile_lds<P_KMAJOR, C::BM, C::NW, POL>(jb.P, jb.ldp, i0, (kt + 1) * kBK, np, wave, lane);
+            load_tile_lds<Q_KMAJOR, C::BN, C::NW, POL>(jb.Q, jb.ldq, j0, (kt + 1) * kBK, np + C::BM * kBK, wave, lane);
+        }
+#pragma unroll
+        for (int kk = 0; kk < kBK / 16; ++kk) {
+            const int fb = kk & 1, nb = fb ^ 1;
+            if (kk + 1 < kBK / 16) {
+#pragma unroll
+                for (int a = 0; a < C::FM; ++a)
+                    pf[nb][a] = read_frag_fast<P_KMAJOR, C::BM>(lp, wm * C::TM + a * 32, kk + 1, lane);
+#pragma unroll
+                for (int b = 0; b < C::FN; ++b)
+                    qf[nb][b] = read_frag_fast<Q_KMAJOR, C::BN>(lp + C::BM * kBK, wn * C::TN + b * 32, kk + 1, lane);
+            } else if (more) {
+                // every wave's reads of this stage are done and the next stage has landed
+                __builtin_amdgcn_s_waitcnt(0);
+                __builtin_amdgcn_s_barrier();
+                const uint16_t* np = smem + (cur ^ 1) * C::STAGE;
+#pragma unroll
+                for (int a = 0; a < C::FM; ++a)
+                    pf[nb][a] = read_frag_fast<P_KMAJOR, C::BM>(np, wm * C::TM + a * 32, 0, lane);
+#pragma unroll
+                for (int b = 0; b < C::FN; ++b)
+                    qf[nb][b] = read_frag_fast<Q_KMAJOR, C::BN>(np + C::BM * kBK, wn * C::TN + b * 32, 0, lane);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int a = 0; a < C::FM; ++a)
+#pragma unroll
+                for (int b = 0; b < C::FN; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[fb][b], pf[fb][a], acc[a][b], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // ---- epilogue, staged through LDS so that every global access is a full coalesced row:
+    //   1. (polynomial, update) the aux tile A or X is copied into LDS with buffer_load ... lds;
+    //   2. each lane computes y for its accumulators (lane holds C[i][j..j+3] for
+    //      i = i_base + lane%32, j = j_base + 8g + 4*(lane/32)), reading aux from LDS and
+    //      writing y in place;
+    //   3. the tile is stored row by row with 16-byte stores;
+    //   4. off-diagonal symmetric tiles are re-staged transposed and stored the same way.
+    // Tile rows hold BN/8 16-byte chunks; chunk c of row i sits at chunk position c ^ (i % CW),
+    // so the 32 rows an accumulator access touches spread over the banks.
+    constexpr int CPRO = C::BN / 8;                     // 16-byte chunks per tile row
+    constexpr int CW = CPRO < 32 ? CPRO : 32;
+    constexpr int CH = C::BM * CPRO;                    // 16-byte chunks per tile
+    static_assert(C::BM == C::BN || EPI == EPI_UPDATE, "symmetric tiles are square");
+    static_assert(CH % (64 * C::NW) == 0, "the aux copy splits evenly over the wavefronts");
+    uint16_t* st = smem;                                 // BM x BN bf16 staging tile (fits the ring)
+    auto spos = [&](int i, int c) { return i * C::BN + ((c ^ (i % CW)) << 3); };
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    if (EPI != EPI_GRAM) {
+        // LDS entry e = 64q + lane is row i = e / CPRO, position pc = e % CPRO, which holds
+        // global chunk c = pc ^ (i % CW) of that row
+        constexpr int NI = CH / 64 / C::NW;
+#pragma unroll
+        for (int jq = 0; jq < NI; ++jq) {
+            const int q = wave * NI + jq;
+            const int e = q * 64 + lane;
+            const int i = e / CPRO, c = (e % CPRO) ^ (i % CW);
+            const int elem = (i0 + i) * jb.ldx + j0 + c * 8;
+            mb_raw_buffer_load_lds(jb.X, (__attribute__((address_space(3))) uint32_t*)(st + q * 512), 16, elem * 2, 0,
+                                   0, POL);
+        }
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+    }
+    uint32_t yb[C::FM][C::FN][4][2];                     // y, packed bf16 pairs (kept for the transposed copy)
+#pragma unroll
+    for (int a = 0; a < C::FM; ++a) {
+        const int i = wm * C::TM + a * 32 + (lane & 31);
+#pragma unroll
+        for (int b = 0; b < C::FN; ++b) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int j = wn * C::TN + b * 32 + 8 * g + 4 * (lane >> 5);
+                uint16_t* p = st + spos(i, j >> 3) + (j & 4);
+                float av[4] = {0.f, 0.f, 0.f, 0.f};
+                if (EPI != EPI_GRAM) {
+                    const u32x2 wv = *reinterpret_cast<const u32x2*>(p);
+                    av[0] = __uint_as_float(wv[0] << 16);
+                    av[1] = __uint_as_float(wv[0] & 0xFFFF0000u);
+                    av[2] = __uint_as_float(wv[1] << 16);
+                    av[3] = __uint_as_float(wv[1] & 0xFFFF0000u);
+                }
+                float y[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float x = acc[a][b][4 * g + r];
+                    if (EPI == EPI_GRAM) y[r] = jb.sig * x;
+                    else if (EPI == EPI_POLY) y[r] = __fmaf_rn(jb.beta, av[r], jb.alpha * x);
+                    else y[r] = jb.sig * __fmaf_rn(jb.beta, av[r], x);
+                }
+                u32x2 wv;
+                wv[0] = f32x2_to_bf16x2_rne(y[0], y[1]);
+                wv[1] = f32x2_to_bf16x2_rne(y[2], y[3]);
+                *reinterpret_cast<u32x2*>(p) = wv;
+                yb[a][b][g][0] = wv[0];
+                yb[a][b][g][1] = wv[1];
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+#pragma unroll 4
+    for (int v = tid; v < CH; v += C::NT) {
+        const int i = v / CPRO, c = v % CPRO;
+        *reinterpret_cast<u32x4*>(jb.out + (int64_t)(i0 + i) * jb.ldo + j0 + c * 8) =
+            *reinterpret_cast<const u32x4*>(st + spos(i, c));
+    }
+    if (EPI != EPI_UPDATE && jb.mirror) {
+        // y^T: lane's y(i, j..j+3) goes to rows j..j+3, column i of the transposed tile
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int a = 0; a < C::FM; ++a) {
+            const int i = wm * C::TM + a * 32 + (lane & 31);
+#pragma unroll
+            for (int b = 0; b < C::FN; ++b) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int j = wn * C::TN + b * 32 + 8 * g + 4 * (lane >> 5);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        st[spos(j + r, i >> 3) + (i & 7)] = (uint16_t)(yb[a][b][g][r >> 1] >> (16 * (r & 1)));
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
+#pragma unroll 4
+        for (int v = tid; v < CH; v += C::NT) {
+            const int jr = v / CPRO, c = v % CPRO;
+            *reinterpret_cast<u32x4*>(jb.out + (int64_t)(j0 + jr) * jb.ldo + i0 + c * 8) =
+                *reinterpret_cast<const u32x4*>(st + spos(jr, c));
+        }
+    }
+}
+
+}  // namespace mb

@@ -176,3 +176,73 @@ def test_ns_transpose_equivariance():
     xt = np.ascontiguousarray(x.transpose(0, 2, 1))
     yt = vals(bits(api.ns_orthogonalize_batched(to_dev(xt))))
     assert np.all(rel_fro(yt.transpose(0, 2, 1), y) <= NS_TOL)
+
+
+# ---------------------------------------------------------------------------
+# Newton-Schulz: persistent (one launch per bank) vs one launch per contraction
+# ---------------------------------------------------------------------------
+# Both schedules run the same tile arithmetic with the same per-element k order
+# (MFMA blocks of 16 in increasing k) and the same epilogue, so their outputs
+# must agree bit for bit; the oracle bound is checked as well.
+
+PERSIST_SHAPES = [(8, 256, 256), (3, 256, 256), (17, 256, 256), (9, 256, 512), (5, 512, 256), (2, 768, 768),
+                  (1, 256, 1024), (2, 1024, 256), (3, 768, 1280),
+                  # sides multiples of 128 but not of 256: 128x128 tiles, two workgroups per CU
+                  (6, 384, 384), (9, 128, 128), (3, 128, 640), (2, 640, 384)]
+
+
+def _ns_per_round(dx, **kw):
+    prev = api.mb_ns_set_path(1)
+    try:
+        return bits(api.ns_orthogonalize_batched(dx, **kw))
+    finally:
+        api.mb_ns_set_path(prev)
+
+
+@pytest.mark.parametrize("shape", PERSIST_SHAPES)
+def test_ns_persistent_bitwise_and_oracle(shape):
+    say(f"ns persistent {shape}")
+    x = random_bf16_matrices(7 + sum(shape), *shape, scale=1e-3)
+    if shape[0] >= 3:
+        x[1] = 0      # a dead slot inside the batch
+    dx = to_dev(x)
+    ref = _ns_per_round(dx)
+    got = bits(api.ns_orthogonalize_batched(dx))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got, ref)
+    if shape[0] >= 3:
+        assert np.all(got[1] == 0)
+    if shape[1] * shape[2] <= 768 * 768:
+        err = rel_fro(vals(got), oracle.newton_schulz(vals(x)))
+        say(f"  rel err per slot: {np.array2string(err, precision=4)}")
+        assert np.all(err <= NS_TOL), err
+
+
+@pytest.mark.parametrize("steps", [1, 2, 3])
+def test_ns_persistent_steps(steps):
+    say(f"ns persistent steps={steps}")
+    x = random_bf16_matrices(40 + steps, 6, 256, 512)
+    dx = to_dev(x)
+    ref = _ns_per_round(dx, steps=steps)
+    got = bits(api.ns_orthogonalize_batched(dx, steps=steps))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_ns_persistent_in_place_and_repeat():
+    say("ns persistent in place / repeat")
+    x = random_bf16_matrices(50, 10, 512, 256)
+    ref = _ns_per_round(to_dev(x))
+    for steps in (5, 1):
+        want = _ns_per_round(to_dev(x), steps=steps)
+        dx = to_dev(x)
+        api.ns_orthogonalize_batched(dx, dx, steps=steps)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(dx), want)
+    # the same workspace reused by back-to-back calls on one stream
+    dx = to_dev(x)
+    ws = torch.empty(api.lib().mb_ns_workspace_bytes(*x.shape), dtype=torch.uint8, device="cuda")
+    outs = [api.ns_orthogonalize_batched(dx, workspace=ws) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs:
+        np.testing.assert_array_equal(bits(o), ref)
