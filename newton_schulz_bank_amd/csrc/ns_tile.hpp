@@ -228,7 +228,9 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, uint16_t* smem, int
     //      i = i_base + lane%32, j = j_base + 8g + 4*(lane/32)), reading aux from LDS and
     //      writing y in place;
     //   3. the tile is stored row by row with 16-byte stores;
-    //   4. off-diagonal symmetric tiles are re-staged transposed and stored the same way.
+    //   4. off-diagonal symmetric tiles are also stored transposed: transposing LDS reads
+    //      (ds_read_b64_tr_b16) of the same staged tile hand each lane 8 consecutive
+    //      elements of a transposed row, stored with one 16-byte store.
     // Tile rows hold BN/8 16-byte chunks; chunk c of row i sits at chunk position c ^ (i % CW),
     // so the 32 rows an accumulator access touches spread over the banks.
     constexpr int CPRO = C::BN / 8;                     // 16-byte chunks per tile row
@@ -256,7 +258,6 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, uint16_t* smem, int
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
     }
-    uint32_t yb[C::FM][C::FN][4][2];                     // y, packed bf16 pairs (kept for the transposed copy)
 #pragma unroll
     for (int a = 0; a < C::FM; ++a) {
         const int i = wm * C::TM + a * 32 + (lane & 31);
@@ -286,8 +287,6 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, uint16_t* smem, int
                 wv[0] = f32x2_to_bf16x2_rne(y[0], y[1]);
                 wv[1] = f32x2_to_bf16x2_rne(y[2], y[3]);
                 *reinterpret_cast<u32x2*>(p) = wv;
-                yb[a][b][g][0] = wv[0];
-                yb[a][b][g][1] = wv[1];
             }
         }
     }
@@ -300,30 +299,28 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, uint16_t* smem, int
             *reinterpret_cast<const u32x4*>(st + spos(i, c));
     }
     if (EPI != EPI_UPDATE && jb.mirror) {
-        // y^T: lane's y(i, j..j+3) goes to rows j..j+3, column i of the transposed tile
-        __builtin_amdgcn_s_waitcnt(0);
-        __builtin_amdgcn_s_barrier();
-#pragma unroll
-        for (int a = 0; a < C::FM; ++a) {
-            const int i = wm * C::TM + a * 32 + (lane & 31);
-#pragma unroll
-            for (int b = 0; b < C::FN; ++b) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int j = wn * C::TN + b * 32 + 8 * g + 4 * (lane >> 5);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        st[spos(j + r, i >> 3) + (i & 7)] = (uint16_t)(yb[a][b][g][r >> 1] >> (16 * (r & 1)));
-                }
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        __builtin_amdgcn_s_barrier();
+        // unit (ib, jb16): tile rows [32 ib, 32 ib + 32) x columns [16 jb16, 16 jb16 + 16); the four
+        // 16-lane groups of a wave take 8 rows each.  In a group, lane 4s + q addresses row s
+        // (then s + 4) at columns 4q..4q+3, and lane t receives column t of those rows: elements
+        // (i..i+7, j + t) = transposed row j + t, columns i..i+7.
+        constexpr int UNITS = (C::BM / 32) * (C::BN / 16);
+        static_assert(UNITS % C::NW == 0, "transposed units split evenly over the wavefronts");
+        const int grp = lane >> 4, t16 = lane & 15, s4 = t16 >> 2, q4 = t16 & 3;
 #pragma unroll 4
-        for (int v = tid; v < CH; v += C::NT) {
-            const int jr = v / CPRO, c = v % CPRO;
-            *reinterpret_cast<u32x4*>(jb.out + (int64_t)(j0 + jr) * jb.ldo + i0 + c * 8) =
-                *reinterpret_cast<const u32x4*>(st + spos(jr, c));
+        for (int u = wave; u < UNITS; u += C::NW) {
+            const int ib = u % (C::BM / 32), jb16 = u / (C::BM / 32);
+            const int i = ib * 32 + grp * 8;
+            const int jc = jb16 * 16 + 4 * q4;
+            const uint16_t* pa = st + spos(i + s4, jc >> 3) + (jc & 7);
+            const uint16_t* pb = st + spos(i + 4 + s4, jc >> 3) + (jc & 7);
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MB_LDS i16x4*)(pa));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MB_LDS i16x4*)(pb));
+            u32x4 w;
+            w[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+            w[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+            w[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+            w[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+            *reinterpret_cast<u32x4*>(jb.out + (int64_t)(j0 + jb16 * 16 + t16) * jb.ldo + i0 + i) = w;
         }
     }
 }
