@@ -154,8 +154,9 @@ int32_t mb_ns_set_path(int32_t path);
 /* Kernel timing (off by default).  While enabled, every kernel the library
  * launches is bracketed by two hipEvents on its stream; mb_timing_read waits
  * for them and returns, per kernel name, the launch count and the summed
- * duration in milliseconds.  Enabling or reading allocates host-side event
- * objects only; it does not change any result. */
+ * duration in milliseconds.  Enabling creates a pool of events that reads hand
+ * back, so a timed loop records events without creating them.  Timing never
+ * changes a result. */
 typedef struct {
     char name[48];
     int64_t launches;

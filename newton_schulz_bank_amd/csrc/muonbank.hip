@@ -47,6 +47,20 @@ struct TimedLaunch {
 std::mutex g_timing_mu;
 bool g_timing_on = false;
 std::vector<TimedLaunch> g_timed;
+// Events are pooled: created when timing is switched on (and on demand), handed back by
+// mb_timing_read, so a timed loop records events without creating any.
+std::vector<hipEvent_t> g_event_pool;
+constexpr size_t kEventPoolInit = 16384;
+
+bool take_event(hipEvent_t* e) {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    if (!g_event_pool.empty()) {
+        *e = g_event_pool.back();
+        g_event_pool.pop_back();
+        return true;
+    }
+    return hipEventCreate(e) == hipSuccess;
+}
 
 struct Timer final : mb::RoundTimer {
     TimedLaunch cur;
@@ -54,7 +68,8 @@ struct Timer final : mb::RoundTimer {
     void begin(const char* name, hipStream_t stream) override {
         if (!g_timing_on) return;
         cur.name = name;
-        if (hipEventCreate(&cur.start) != hipSuccess || hipEventCreate(&cur.stop) != hipSuccess) return;
+        if (!take_event(&cur.start)) return;
+        if (!take_event(&cur.stop)) return;
         (void)hipEventRecord(cur.start, stream);
         open = true;
     }
@@ -533,6 +548,11 @@ int32_t mb_ns_set_path(int32_t path) {
 void mb_timing_enable(int32_t on) {
     std::lock_guard<std::mutex> lk(g_timing_mu);
     g_timing_on = on != 0;
+    while (g_timing_on && g_event_pool.size() < kEventPoolInit) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) break;
+        g_event_pool.push_back(e);
+    }
 }
 
 int32_t mb_timing_read(mb_kernel_time* out, int32_t max_entries) {
@@ -546,8 +566,11 @@ int32_t mb_timing_read(mb_kernel_time* out, int32_t max_entries) {
     for (auto& t : launches) {
         float ms = 0.f;
         if (hipEventSynchronize(t.stop) != hipSuccess || hipEventElapsedTime(&ms, t.start, t.stop) != hipSuccess) rc = -1;
-        (void)hipEventDestroy(t.start);
-        (void)hipEventDestroy(t.stop);
+        {
+            std::lock_guard<std::mutex> lk(g_timing_mu);
+            g_event_pool.push_back(t.start);
+            g_event_pool.push_back(t.stop);
+        }
         size_t k = 0;
         for (; k < agg.size(); ++k)
             if (t.name == agg[k].name) break;
