@@ -211,7 +211,7 @@ def frobenius_prescale(x, eps: float = NS_EPS) -> np.ndarray:
 
 
 def newton_schulz(u, steps: int = NS_STEPS, a: float = NS_COEFFS[0], b: float = NS_COEFFS[1],
-                  c: float = NS_COEFFS[2], eps: float = NS_EPS) -> np.ndarray:
+                  c: float = NS_COEFFS[2], eps: float = NS_EPS, schedule=None) -> np.ndarray:
     """Quintic Newton-Schulz on every slot of u [batch, rows, cols].
 
     Per slot: work on X = u (or u^T when rows > cols, so that the Gram matrix
@@ -220,7 +220,16 @@ def newton_schulz(u, steps: int = NS_STEPS, a: float = NS_COEFFS[0], b: float = 
     the odd quintic a*s + b*s^3 + c*s^5 on the singular values ("Muon Custom
     Sizing", section 2.3: coefficients 3.4445, -4.7750, 2.0315, five rounds;
     Record 7 page, section 4.2: five quintic iterations).  Transposed back at
-    the end.  float64 throughout."""
+    the end.  float64 throughout.
+
+    ``schedule``, if given, is a sequence of (a, b, c), one per round: round t
+    uses its own coefficients and the number of rounds is len(schedule).  The
+    pages name orthogonalizers with per-round coefficients ("Unified zero-copy
+    optimizer" page, sections 1.3 and 4) without printing any; the round itself
+    is the same map."""
+    if schedule is None:
+        schedule = [(a, b, c)] * steps
+    schedule = [tuple(float(v) for v in abc) for abc in schedule]
     u = np.asarray(u, dtype=np.float64)
     out = np.empty_like(u)
     for i in range(u.shape[0]):
@@ -229,10 +238,10 @@ def newton_schulz(u, steps: int = NS_STEPS, a: float = NS_COEFFS[0], b: float = 
         if tall:
             x = x.T
         x = frobenius_prescale(x, eps)
-        for _ in range(steps):
+        for (ra, rb, rc) in schedule:
             gram = x @ x.T
-            poly = b * gram + c * (gram @ gram)
-            x = a * x + poly @ x
+            poly = rb * gram + rc * (gram @ gram)
+            x = ra * x + poly @ x
         out[i] = x.T if tall else x
     return out
 
@@ -287,7 +296,7 @@ def muon_bank_step(grad, buf, w_hi, w_lo, storage: str, *, lr: float = 0.02,
                    weight_decay: float = 0.01, momentum: float = 0.95,
                    lr_mul: float = 1.0, wd_mul: float = 1.0, lr_mul_per_slot=None,
                    steps: int = NS_STEPS, a: float = NS_COEFFS[0], b: float = NS_COEFFS[1],
-                   c: float = NS_COEFFS[2], eps: float = NS_EPS) -> dict:
+                   c: float = NS_COEFFS[2], eps: float = NS_EPS, schedule=None) -> dict:
     """One Muon step on a viewed bank [batch, rows, cols].
 
     grad and buf are float64 arrays of values of the storage format (fp32 or
@@ -300,7 +309,7 @@ def muon_bank_step(grad, buf, w_hi, w_lo, storage: str, *, lr: float = 0.02,
     _, rows, cols = grad.shape
     sc = step_scalars(lr, weight_decay, momentum, rows, cols, lr_mul, wd_mul)
     buf_new, u = momentum_nesterov(grad, buf, sc.mu, sc.nu, storage)
-    v64 = newton_schulz(u, steps, a, b, c, eps)
+    v64 = newton_schulz(u, steps, a, b, c, eps, schedule=schedule)
     v = round_to_bf16(v64)
     if lr_mul_per_slot is None:
         eta = sc.eta

@@ -156,3 +156,60 @@ def test_frobenius_prescale_matches_library_norm():
     x = np.random.default_rng(2).normal(0, 3, (17, 29))
     np.testing.assert_allclose(frobenius_prescale(x, 0.0), x / np.linalg.norm(x, "fro"), rtol=1e-14)
     assert np.all(frobenius_prescale(np.zeros((3, 3))) == 0.0)
+
+
+# ---------------------------------------------------------------------------
+# per-round coefficient schedules
+# ---------------------------------------------------------------------------
+# With round t using p_t(s) = a_t s + b_t s^3 + c_t s^5, the rounds map the scaled
+# singular values through the composition p_T o ... o p_1 (each round is an odd
+# matrix polynomial, acting on singular values).
+
+SCHEDULE = [(3.4445, -4.7750, 2.0315), (3.0, -3.2, 1.2), (2.0, -1.5, 0.5), (1.875, -1.25, 0.375),
+            (1.5, -0.5, 0.0)]
+
+
+def closed_form_schedule(x, schedule):
+    u, s, vt = np.linalg.svd(x, full_matrices=False)
+    s = s / (np.linalg.norm(x) + EPS)
+    for (ra, rb, rc) in schedule:
+        s = ra * s + rb * s ** 3 + rc * s ** 5
+    return (u * s) @ vt
+
+
+@pytest.mark.parametrize("shape", [(8, 8), (6, 12), (12, 6), (1, 12), (5, 20)])
+def test_schedule_equals_composed_closed_form(shape):
+    rng = np.random.default_rng(100 + sum(shape))
+    x = rng.normal(0, 1, (2,) + shape)
+    got = newton_schulz(x, eps=EPS, schedule=SCHEDULE)
+    for i in range(2):
+        np.testing.assert_allclose(got[i], closed_form_schedule(x[i], SCHEDULE), rtol=0, atol=1e-10)
+
+
+def test_schedule_order_matters_and_constant_schedule_is_the_fixed_round():
+    rng = np.random.default_rng(101)
+    x = rng.normal(0, 1, (1, 9, 7))
+    fwd = newton_schulz(x, eps=EPS, schedule=SCHEDULE)
+    rev = newton_schulz(x, eps=EPS, schedule=SCHEDULE[::-1])
+    assert np.abs(fwd - rev).max() > 1e-3
+    np.testing.assert_array_equal(newton_schulz(x, 5, A, B, C, EPS, schedule=[(A, B, C)] * 5),
+                                  newton_schulz(x, 5, A, B, C, EPS))
+
+
+def test_identity_rounds_leave_x_unchanged():
+    """(1, 0, 0) is the identity polynomial: appending such rounds changes nothing."""
+    rng = np.random.default_rng(102)
+    x = rng.normal(0, 1, (2, 6, 10))
+    one = newton_schulz(x, 1, A, B, C, EPS)
+    np.testing.assert_allclose(newton_schulz(x, eps=EPS, schedule=[(A, B, C), (1, 0, 0), (1, 0, 0)]), one,
+                               rtol=0, atol=1e-15)
+
+
+def test_one_row_slot_with_schedule_in_exact_rationals():
+    rng = np.random.default_rng(103)
+    g = rng.normal(0, 1e-3, (1, 1, 12))
+    nrm = float(np.linalg.norm(g))
+    s = Fraction(nrm) / (Fraction(nrm) + Fraction(EPS))
+    for (ra, rb, rc) in SCHEDULE:
+        s = Fraction(ra) * s + Fraction(rb) * s ** 3 + Fraction(rc) * s ** 5
+    np.testing.assert_allclose(newton_schulz(g, schedule=SCHEDULE)[0], float(s) * g[0] / nrm, rtol=1e-12, atol=0)
