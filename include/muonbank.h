@@ -70,6 +70,12 @@ typedef struct {
     int32_t ns_steps;
     double a, b, c;
     double eps;
+    /* Optional per-round coefficients: NULL (the default) applies (a, b, c) in
+     * every round; otherwise a host array of 3*ns_steps doubles, (a_t, b_t, c_t)
+     * for round t, read during the call only.  Orthogonalizers with per-round
+     * coefficients are named on the "Unified zero-copy optimizer" page
+     * (sections 1.3, 4) without values, so the caller supplies them. */
+    const double *ns_schedule;
 } mb_hparams;
 
 /* One viewed bank [batch, rows, cols] (e.g. attention QKVO (10, 3072, 768)
@@ -128,6 +134,16 @@ mb_status ns_orthogonalize_batched(const uint16_t *x, uint16_t *y,
                                    int64_t batch, int64_t rows, int64_t cols,
                                    int32_t steps, double a, double b, double c, double eps,
                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* ns_orthogonalize_batched with per-round coefficients: round t (0-based) uses
+ * schedule[3t], schedule[3t+1], schedule[3t+2] as (a, b, c); `schedule` is a
+ * host array of 3*steps finite doubles (NULL is MB_ERR_NULL), read during the
+ * call only.  Same workspace as ns_orthogonalize_batched.  Each coefficient is
+ * rounded once to float32 for the kernels. */
+mb_status ns_orthogonalize_batched_sched(const uint16_t *x, uint16_t *y,
+                                         int64_t batch, int64_t rows, int64_t cols,
+                                         int32_t steps, const double *schedule, double eps,
+                                         void *workspace, size_t workspace_bytes, void *stream);
 
 /* Stage 3 alone (Record 7 walkthrough, section 4.1): on every element of
  * [batch, slot_numel], w = fp32(w_hi << 16 | w_lo); t = RN32(w*decay);

@@ -27,6 +27,9 @@ _STATUS = {0: "MB_OK", 1: "MB_ERR_NULL", 2: "MB_ERR_SHAPE", 3: "MB_ERR_DTYPE", 4
            5: "MB_ERR_WORKSPACE", 6: "MB_ERR_ALIAS", 7: "MB_ERR_VALUE", 8: "MB_ERR_HIP"}
 
 
+vp_t = ctypes.c_void_p
+
+
 class MuonBankError(RuntimeError):
     def __init__(self, status: int, message: str):
         self.status = status
@@ -37,7 +40,7 @@ class MuonBankError(RuntimeError):
 class mb_hparams(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_double), ("weight_decay", ctypes.c_double), ("momentum", ctypes.c_double),
                 ("ns_steps", ctypes.c_int32), ("a", ctypes.c_double), ("b", ctypes.c_double),
-                ("c", ctypes.c_double), ("eps", ctypes.c_double)]
+                ("c", ctypes.c_double), ("eps", ctypes.c_double), ("ns_schedule", ctypes.c_void_p)]
 
 
 class mb_bank(ctypes.Structure):
@@ -56,7 +59,7 @@ _lib = None
 
 EXPORTED = ("mb_default_hparams", "mb_status_string", "mb_last_error", "mb_version", "mb_step_workspace_bytes",
             "mb_ns_workspace_bytes", "muon_bank_step", "muon_momentum_update", "ns_orthogonalize_batched",
-            "mp_apply_update", "mb_ns_set_path", "mb_timing_enable", "mb_timing_read")
+            "ns_orthogonalize_batched_sched", "mp_apply_update", "mb_ns_set_path", "mb_timing_enable", "mb_timing_read")
 
 
 def lib() -> ctypes.CDLL:
@@ -79,6 +82,7 @@ def lib() -> ctypes.CDLL:
         "muon_bank_step": (i32, [ctypes.POINTER(mb_bank), i32, ctypes.POINTER(mb_hparams), vp, sz, vp]),
         "muon_momentum_update": (i32, [vp, vp, vp, i64, i64, i64, i32, f32, f32, vp]),
         "ns_orthogonalize_batched": (i32, [vp, vp, i64, i64, i64, i32, f64, f64, f64, f64, vp, sz, vp]),
+        "ns_orthogonalize_batched_sched": (i32, [vp, vp, i64, i64, i64, i32, vp, f64, vp, sz, vp]),
         "mp_apply_update": (i32, [vp, vp, vp, i64, i64, f32, f32, vp, vp]),
         "mb_ns_set_path": (i32, [i32]),
         "mb_timing_enable": (None, [i32]),
@@ -125,12 +129,28 @@ def default_hparams() -> mb_hparams:
     return hp
 
 
-def make_hparams(**kw) -> mb_hparams:
+def _schedule_array(schedule):
+    """[(a, b, c), ...] -> a ctypes array of 3*len doubles."""
+    flat = [float(v) for abc in schedule for v in abc]
+    if len(flat) != 3 * len(schedule) or not schedule:
+        raise ValueError("schedule must be a non-empty sequence of (a, b, c)")
+    return (ctypes.c_double * len(flat))(*flat)
+
+
+def make_hparams(schedule=None, **kw) -> mb_hparams:
+    """mb_hparams with the library defaults, overridden by keyword; ``schedule`` = [(a, b, c), ...]
+    sets per-round coefficients (and ns_steps to its length).  The returned struct keeps the
+    schedule array alive."""
     hp = default_hparams()
     for k, v in kw.items():
-        if not hasattr(hp, k):
+        if not hasattr(hp, k) or k == "ns_schedule":
             raise KeyError(k)
         setattr(hp, k, v)
+    if schedule is not None:
+        arr = _schedule_array(schedule)
+        hp.ns_steps = len(schedule)
+        hp.ns_schedule = ctypes.cast(arr, ctypes.c_void_p)
+        hp._schedule_keepalive = arr
     return hp
 
 
@@ -225,8 +245,9 @@ def muon_momentum_update(grad: torch.Tensor, momentum: torch.Tensor, u_out: torc
 
 def ns_orthogonalize_batched(x: torch.Tensor, y: torch.Tensor | None = None, steps: int = 5, a: float = 3.4445,
                              b: float = -4.7750, c: float = 2.0315, eps: float = 1e-7,
-                             workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """y = NS(x) for bf16 [batch, rows, cols]; returns y (a new tensor if none is given)."""
+                             workspace: torch.Tensor | None = None, stream=None, schedule=None) -> torch.Tensor:
+    """y = NS(x) for bf16 [batch, rows, cols]; returns y (a new tensor if none is given).
+    ``schedule`` = [(a, b, c), ...] gives every round its own coefficients (steps = its length)."""
     _dense(x, "x", 2)
     if x.dim() != 3:
         raise ValueError("x must be [batch, rows, cols]")
@@ -237,6 +258,12 @@ def ns_orthogonalize_batched(x: torch.Tensor, y: torch.Tensor | None = None, ste
         raise ValueError("y must have x's shape")
     bt, r, cc = x.shape
     ws = _workspace(int(lib().mb_ns_workspace_bytes(bt, r, cc)), x, workspace)
+    if schedule is not None:
+        arr = _schedule_array(schedule)
+        _check(lib().ns_orthogonalize_batched_sched(_ptr(x), _ptr(y), bt, r, cc, len(schedule), ctypes.cast(arr, vp_t),
+                                                    float(eps), ws.data_ptr(), ws.numel() * ws.element_size(),
+                                                    _stream(stream)))
+        return y
     _check(lib().ns_orthogonalize_batched(_ptr(x), _ptr(y), bt, r, cc, int(steps), float(a), float(b), float(c),
                                           float(eps), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
     return y

@@ -46,6 +46,12 @@ struct NsRound {
 };
 hipError_t ns_round(const NsRound& r, hipStream_t stream, RoundTimer* timer);
 
+// Coefficients of one Newton-Schulz round, X' = a*X + (b*A + c*A A) X.
+struct NsCoef {
+    float a, b, c;
+};
+constexpr int kMaxRounds = 64;
+
 // Every Newton-Schulz round of a bank in one persistent launch (x0 -> ... -> dest), with xa, xb
 // as ping-pong buffers, A and Bm as scratch and sync (ns_persist_sync_ints ints, cleared by
 // launch_ns_scale) for the task queues and per-slot counters.
@@ -60,8 +66,8 @@ struct NsPersist {
     const int* live;
     int* sync;
     int64_t batch, rows, cols;
-    int steps;
-    float a, b, c;
+    int steps;              // 1..kMaxRounds
+    const NsCoef* coef;     // host array of `steps` rounds
 };
 bool ns_persist_eligible(int64_t rows, int64_t cols, int steps);
 int ns_persist_sync_ints(int64_t batch);

@@ -166,11 +166,19 @@ mb_status check_no_overlap(const std::vector<Range>& rs) {
 
 bool is_finite(double v) { return std::isfinite(v); }
 
+mb_status check_schedule(const double* schedule, int steps, const char* what) {
+    for (int i = 0; schedule && i < 3 * steps; ++i)
+        if (!is_finite(schedule[i])) return fail(MB_ERR_VALUE, "%s: schedule entry %d is not finite", what, i);
+    return MB_OK;
+}
+
 mb_status check_hparams(const mb_hparams& hp) {
     if (!is_finite(hp.lr) || !is_finite(hp.weight_decay) || !is_finite(hp.momentum) || !is_finite(hp.a) || !is_finite(hp.b) ||
         !is_finite(hp.c) || !is_finite(hp.eps))
         return fail(MB_ERR_VALUE, "hyper-parameters must be finite");
-    if (hp.ns_steps < 1 || hp.ns_steps > 64) return fail(MB_ERR_VALUE, "ns_steps must be in 1..64 (got %d)", hp.ns_steps);
+    if (hp.ns_steps < 1 || hp.ns_steps > mb::kMaxRounds)
+        return fail(MB_ERR_VALUE, "ns_steps must be in 1..%d (got %d)", mb::kMaxRounds, hp.ns_steps);
+    if (check_schedule(hp.ns_schedule, hp.ns_steps, "hparams") != MB_OK) return MB_ERR_VALUE;
     if (hp.eps < 0) return fail(MB_ERR_VALUE, "eps must be >= 0");
     return MB_OK;
 }
@@ -211,11 +219,22 @@ std::atomic<int> g_ns_path{0};
 // Newton-Schulz rounds on scaled input: x_first -> ... -> dest.  x1, x2 are ping-pong buffers
 // distinct from x_first and dest; sync (cleared by the ns_scale launch) serves the persistent
 // kernel.
+// The per-round coefficients, each rounded once to float32: the schedule (3*steps doubles) if
+// given, else (a, b, c) in every round.
+std::vector<mb::NsCoef> ns_coefs(int steps, double a, double b, double c, const double* schedule) {
+    std::vector<mb::NsCoef> v((size_t)steps);
+    for (int t = 0; t < steps; ++t)
+        v[(size_t)t] = schedule ? mb::NsCoef{f32(schedule[3 * t]), f32(schedule[3 * t + 1]), f32(schedule[3 * t + 2])}
+                                : mb::NsCoef{f32(a), f32(b), f32(c)};
+    return v;
+}
+
 mb_status run_ns(const uint16_t* x_first, uint16_t* dest, uint16_t* x1, uint16_t* x2, uint16_t* A, uint16_t* Bm,
-                 int64_t batch, int64_t rows, int64_t cols, int steps, double a, double b, double c,
+                 int64_t batch, int64_t rows, int64_t cols, const std::vector<mb::NsCoef>& coef,
                  const float* scale, const int* live, int* sync, hipStream_t stream, Timer& timer) {
+    const int steps = (int)coef.size();
     if (g_ns_path.load() == 0 && mb::ns_persist_eligible(rows, cols, steps)) {
-        mb::NsPersist r{x_first, x1, x2, dest, A, Bm, scale, live, sync, batch, rows, cols, steps, f32(a), f32(b), f32(c)};
+        mb::NsPersist r{x_first, x1, x2, dest, A, Bm, scale, live, sync, batch, rows, cols, steps, coef.data()};
         timer.begin("ns_persist", stream);
         hipError_t e = mb::ns_persist(r, stream);
         timer.end(stream);
@@ -226,7 +245,8 @@ mb_status run_ns(const uint16_t* x_first, uint16_t* dest, uint16_t* x1, uint16_t
     for (int s = 0; s < steps; ++s) {
         const bool last = s == steps - 1;
         uint16_t* out = last ? dest : ((s & 1) ? x2 : x1);
-        mb::NsRound r{in, out, A, Bm, batch, rows, cols, f32(a), f32(b), f32(c), s == 0, scale, live};
+        const mb::NsCoef& k = coef[(size_t)s];
+        mb::NsRound r{in, out, A, Bm, batch, rows, cols, k.a, k.b, k.c, s == 0, scale, live};
         hipError_t e = mb::ns_round(r, stream, &timer);
         if (e != hipSuccess) return fail(MB_ERR_HIP, "Newton-Schulz round %d: %s", s, hipGetErrorString(e));
         in = out;
@@ -248,6 +268,7 @@ void mb_default_hparams(mb_hparams* hp) {
     hp->b = -4.7750;
     hp->c = 2.0315;
     hp->eps = 1e-7;
+    hp->ns_schedule = nullptr;
 }
 
 const char* mb_status_string(int32_t s) {
@@ -311,17 +332,23 @@ mb_status muon_momentum_update(const void* grad, void* momentum, uint16_t* u_out
     return ok();
 }
 
-mb_status ns_orthogonalize_batched(const uint16_t* x, uint16_t* y, int64_t batch, int64_t rows, int64_t cols,
-                                   int32_t steps, double a, double b, double c, double eps, void* workspace,
-                                   size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+mb_status ns_orthogonalize_impl(const uint16_t* x, uint16_t* y, int64_t batch, int64_t rows, int64_t cols,
+                                int32_t steps, double a, double b, double c, const double* schedule, double eps,
+                                void* workspace, size_t workspace_bytes, void* stream) {
     if (!x || !y) return fail(MB_ERR_NULL, "ns_orthogonalize_batched: null tensor pointer");
     mb_status s = check_shape(batch, rows, cols, "ns_orthogonalize_batched");
     if (s != MB_OK) return s;
     if (!aligned16(x) || !aligned16(y) || (workspace && !aligned16(workspace)))
         return fail(MB_ERR_ALIGN, "ns_orthogonalize_batched: pointers must be 16-byte aligned");
-    if (steps < 1 || steps > 64) return fail(MB_ERR_VALUE, "ns_orthogonalize_batched: steps must be in 1..64");
+    if (steps < 1 || steps > mb::kMaxRounds)
+        return fail(MB_ERR_VALUE, "ns_orthogonalize_batched: steps must be in 1..%d", mb::kMaxRounds);
     if (!is_finite(a) || !is_finite(b) || !is_finite(c) || !is_finite(eps) || eps < 0)
         return fail(MB_ERR_VALUE, "ns_orthogonalize_batched: coefficients must be finite and eps >= 0");
+    if (check_schedule(schedule, steps, "ns_orthogonalize_batched") != MB_OK) return MB_ERR_VALUE;
     const bool vec = (rows * cols) % 8 == 0;
     const BankWs L = bank_ws_layout(batch, rows, cols, vec);
     if (!workspace || workspace_bytes < L.total)
@@ -357,14 +384,33 @@ mb_status ns_orthogonalize_batched(const uint16_t* x, uint16_t* y, int64_t batch
     if (e != hipSuccess) return fail(MB_ERR_HIP, "ns_scale launch: %s", hipGetErrorString(e));
     // in place with a single round: write the round to scratch, then copy
     uint16_t* dest = (x == y && steps == 1) ? (uint16_t*)(ws + L.u) : y;
-    s = run_ns(x, dest, x1, x2, (uint16_t*)(ws + L.A), (uint16_t*)(ws + L.Bm), batch, rows, cols, steps, a, b, c,
-               scale, live, sync, st, timer);
+    s = run_ns(x, dest, x1, x2, (uint16_t*)(ws + L.A), (uint16_t*)(ws + L.Bm), batch, rows, cols,
+               ns_coefs(steps, a, b, c, schedule), scale, live, sync, st, timer);
     if (s != MB_OK) return s;
     if (dest != y) {
         e = hipMemcpyAsync(y, dest, n * 2, hipMemcpyDeviceToDevice, st);
         if (e != hipSuccess) return fail(MB_ERR_HIP, "copy: %s", hipGetErrorString(e));
     }
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+mb_status ns_orthogonalize_batched(const uint16_t* x, uint16_t* y, int64_t batch, int64_t rows, int64_t cols,
+                                   int32_t steps, double a, double b, double c, double eps, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    return ns_orthogonalize_impl(x, y, batch, rows, cols, steps, a, b, c, nullptr, eps, workspace, workspace_bytes,
+                                 stream);
+}
+
+mb_status ns_orthogonalize_batched_sched(const uint16_t* x, uint16_t* y, int64_t batch, int64_t rows, int64_t cols,
+                                         int32_t steps, const double* schedule, double eps, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+    if (!schedule) return fail(MB_ERR_NULL, "ns_orthogonalize_batched_sched: null schedule");
+    return ns_orthogonalize_impl(x, y, batch, rows, cols, steps, 1.0, 0.0, 0.0, schedule, eps, workspace,
+                                 workspace_bytes, stream);
 }
 
 mb_status mp_apply_update(uint16_t* w_hi, uint16_t* w_lo, const uint16_t* v, int64_t batch, int64_t slot_numel,
@@ -518,8 +564,8 @@ mb_status muon_bank_step(const mb_bank* banks, int32_t num_banks, const mb_hpara
         if (e != hipSuccess) return fail(MB_ERR_HIP, "ns_scale launch: %s", hipGetErrorString(e));
         // with one round and no v_out, the round would read u while writing v in the same buffer
         uint16_t* dest = (hp.ns_steps == 1 && v == u) ? x2 : v;
-        s = run_ns(u, dest, x1, x2, A, Bm, nb, b.rows, b.cols, hp.ns_steps, hp.a, hp.b, hp.c, scale, live, sync, us,
-                   timer);
+        s = run_ns(u, dest, x1, x2, A, Bm, nb, b.rows, b.cols, ns_coefs(hp.ns_steps, hp.a, hp.b, hp.c, hp.ns_schedule),
+                   scale, live, sync, us, timer);
         if (s != MB_OK) return s;
         timer.begin("apply", us);
         e = mb::launch_apply(w_hi, w_lo, dest, nb, slot, vec, eta, decay, lrm, us);

@@ -53,7 +53,7 @@ struct PersistArgs {
     int m, n;               // Gram size and long side (m <= n)
     int tm, tn;             // tiles along m and along n
     int batch, steps, nq;
-    float a, b, c;
+    float coef[kMaxRounds][3];   // (a, b, c) of each round
 };
 
 __device__ __forceinline__ int ld_relaxed(const int* p) {
@@ -163,8 +163,8 @@ __global__ void __launch_bounds__(C::NT, 2) ns_persist_kernel(PersistArgs p) {
                 jb.j0 = tj * kTile;
                 jb.out = Bs;
                 jb.mirror = ti != tj;
-                jb.alpha = p.c;
-                jb.beta = p.b;
+                jb.alpha = p.coef[t][2];
+                jb.beta = p.coef[t][1];
                 gemm_tile<true, true, EPI_POLY, C, POL_SC1>(jb, smem, ltid);
             }
         } else {
@@ -187,7 +187,7 @@ __global__ void __launch_bounds__(C::NT, 2) ns_persist_kernel(PersistArgs p) {
                 jb.j0 = tj * kTile;
                 jb.out = os;
                 jb.mirror = false;
-                jb.beta = p.a;
+                jb.beta = p.coef[t][0];
                 if (t == 0) jb.sig = p.scale[slot];
                 gemm_tile<true, TALL, EPI_UPDATE, C, POL_SC1>(jb, smem, ltid);
             } else if (last) {
@@ -248,7 +248,7 @@ int persist_tile(int64_t m, int64_t n) {
 
 bool ns_persist_eligible(int64_t rows, int64_t cols, int steps) {
     const int64_t m = rows < cols ? rows : cols, n = rows < cols ? cols : rows;
-    return steps >= 1 && persist_tile(m, n) != 0 && m * n <= ((int64_t)1 << 30) && m * m <= ((int64_t)1 << 30);
+    return steps >= 1 && steps <= kMaxRounds && persist_tile(m, n) != 0 && m * n <= ((int64_t)1 << 30) && m * m <= ((int64_t)1 << 30);
 }
 
 int ns_persist_sync_ints(int64_t batch) { return 32 + (int)batch; }
@@ -278,9 +278,11 @@ hipError_t ns_persist(const NsPersist& r, hipStream_t stream) {
     p.batch = (int)r.batch;
     p.steps = r.steps;
     p.nq = d.xccs;
-    p.a = r.a;
-    p.b = r.b;
-    p.c = r.c;
+    for (int t = 0; t < r.steps && t < kMaxRounds; ++t) {
+        p.coef[t][0] = r.coef[t].a;
+        p.coef[t][1] = r.coef[t].b;
+        p.coef[t][2] = r.coef[t].c;
+    }
     if (tile == 256) {
         // one 8-wavefront workgroup per CU (its 128 KiB ring fills the LDS)
         const dim3 grid((unsigned)d.cus);

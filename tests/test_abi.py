@@ -110,6 +110,9 @@ def test_step_validation_errors(L):
     hp.lr = math.nan
     assert _step(L, [good], ws, need, hp) == VALUE
     assert _step(L, [_bank(lr_mul=math.inf)[0]], ws, need) == VALUE
+    hp = api.make_hparams(schedule=[(3.4445, -4.775, 2.0315), (1.0, math.nan, 0.0)])
+    assert _step(L, [good], ws, need, hp) == VALUE
+    assert b"schedule" in L.mb_last_error()
     assert len(L.mb_last_error()) > 0
 
 
@@ -133,6 +136,14 @@ def test_stage_entry_point_validation_errors(L):
     assert L.ns_orthogonalize_batched(p, p + 16, 2, 64, 64, 5, 3.4445, -4.775, 2.0315, 1e-7, ws, need, None) == ALIAS
     assert L.ns_orthogonalize_batched(p, p + (1 << 30), 2, 64, 64, 5, 3.4445, -4.775, 2.0315, 1e-7, p + 256, need, None) == ALIAS
     assert L.ns_orthogonalize_batched(p + 2, p + (1 << 30), 2, 64, 64, 5, 3.4445, -4.775, 2.0315, 1e-7, ws, need, None) == ALIGN
+    # Newton-Schulz with per-round coefficients
+    sched = (ctypes.c_double * 6)(3.4445, -4.775, 2.0315, 3.0, -3.2, 1.2)
+    bad = (ctypes.c_double * 6)(3.4445, -4.775, 2.0315, 3.0, math.inf, 1.2)
+    assert L.ns_orthogonalize_batched_sched(p, p + (1 << 30), 2, 64, 64, 2, None, 1e-7, ws, need, None) == NULL
+    assert L.ns_orthogonalize_batched_sched(p, p + (1 << 30), 2, 64, 64, 2, bad, 1e-7, ws, need, None) == VALUE
+    assert L.ns_orthogonalize_batched_sched(p, p + (1 << 30), 2, 64, 64, 0, sched, 1e-7, ws, need, None) == VALUE
+    assert L.ns_orthogonalize_batched_sched(p, p + (1 << 30), 2, 64, 64, 65, sched, 1e-7, ws, need, None) == VALUE
+    assert L.ns_orthogonalize_batched_sched(p, p + (1 << 30), 2, 64, 64, 2, sched, 1e-7, ws, need - 1, None) == WORKSPACE
     # apply
     assert L.mp_apply_update(None, p, p, 1, 64, 0.02, 0.9998, None, None) == NULL
     assert L.mp_apply_update(p, p + (1 << 30), p + (2 << 30), 1, 0, 0.02, 0.9998, None, None) == SHAPE

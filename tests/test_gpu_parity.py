@@ -246,3 +246,53 @@ def test_ns_persistent_in_place_and_repeat():
     torch.cuda.synchronize()
     for o in outs:
         np.testing.assert_array_equal(bits(o), ref)
+
+
+# ---------------------------------------------------------------------------
+# Newton-Schulz with per-round coefficients
+# ---------------------------------------------------------------------------
+
+SCHEDULE = [(3.4445, -4.7750, 2.0315), (3.0, -3.2, 1.2), (2.0, -1.5, 0.5), (1.875, -1.25, 0.375), (1.5, -0.5, 0.0)]
+
+
+@pytest.mark.parametrize("shape", [(4, 256, 256), (3, 768, 256), (5, 384, 384), (2, 100, 260), (3, 6, 12)])
+def test_ns_schedule_parity(shape):
+    say(f"ns schedule {shape}")
+    x = random_bf16_matrices(60 + sum(shape), *shape, scale=1e-3)
+    want = oracle.newton_schulz(vals(x), schedule=SCHEDULE)
+    dx = to_dev(x)
+    got = bits(api.ns_orthogonalize_batched(dx, schedule=SCHEDULE))
+    torch.cuda.synchronize()
+    err = rel_fro(vals(got), want)
+    say(f"  rel err per slot: {np.array2string(err, precision=4)}")
+    assert np.all(err <= NS_TOL), err
+    np.testing.assert_array_equal(got, _ns_per_round(dx, schedule=SCHEDULE))
+
+
+def test_ns_constant_schedule_equals_plain_call():
+    say("ns constant schedule")
+    x = random_bf16_matrices(70, 4, 256, 512)
+    dx = to_dev(x)
+    plain = bits(api.ns_orthogonalize_batched(dx))
+    sched = bits(api.ns_orthogonalize_batched(dx, schedule=[(3.4445, -4.7750, 2.0315)] * 5))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(plain, sched)
+
+
+def test_bank_step_with_schedule():
+    say("bank step with schedule")
+    bank = make_random_bank(71, 3, 256, 384)
+    dev = api.Bank(grad=to_dev(bank["grad"], True), momentum=to_dev(bank["momentum"], True), w_hi=to_dev(bank["w_hi"]),
+                   w_lo=to_dev(bank["w_lo"]))
+    dev.v_out = torch.empty(bank["w_hi"].shape, dtype=torch.int16, device="cuda")
+    dev.u_out = torch.empty(bank["w_hi"].shape, dtype=torch.int16, device="cuda")
+    api.muon_bank_step([dev], hp=api.make_hparams(schedule=SCHEDULE))
+    torch.cuda.synchronize()
+    u = vals(bits(dev.u_out))
+    want_v = oracle.newton_schulz(u, schedule=SCHEDULE)
+    err = rel_fro(vals(bits(dev.v_out)), want_v)
+    assert np.all(err <= NS_TOL), err
+    sc = oracle.step_scalars(0.02, 0.01, 0.95, 256, 384)
+    want_hi, want_lo = oracle.mp_apply_update(bank["w_hi"], bank["w_lo"], vals(bits(dev.v_out)), sc.eta, sc.decay)
+    np.testing.assert_array_equal(bits(dev.w_hi), want_hi)
+    np.testing.assert_array_equal(bits(dev.w_lo), want_lo)
