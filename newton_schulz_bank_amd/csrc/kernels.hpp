@@ -70,6 +70,20 @@ struct NsPersist {
     const NsCoef* coef;     // host array of `steps` rounds
 };
 bool ns_persist_eligible(int64_t rows, int64_t cols, int steps);
+
+// Every Newton-Schulz round of a bank of small slots (Gram side <= 64, <= 4096 elements) in one
+// launch, one workgroup per slot (x0 -> dest; dest may equal x0).
+struct NsSmall {
+    const uint16_t* x0;
+    uint16_t* dest;
+    const float* scale;
+    const int* live;
+    int64_t batch, rows, cols;
+    int steps;
+    const NsCoef* coef;
+};
+bool ns_small_eligible(int64_t rows, int64_t cols, int steps);
+hipError_t ns_small(const NsSmall& r, hipStream_t stream);
 int ns_persist_sync_ints(int64_t batch);
 hipError_t ns_persist(const NsPersist& r, hipStream_t stream);
 

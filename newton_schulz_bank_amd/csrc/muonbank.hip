@@ -241,6 +241,14 @@ mb_status run_ns(const uint16_t* x_first, uint16_t* dest, uint16_t* x1, uint16_t
         if (e != hipSuccess) return fail(MB_ERR_HIP, "Newton-Schulz launch: %s", hipGetErrorString(e));
         return MB_OK;
     }
+    if (g_ns_path.load() == 0 && mb::ns_small_eligible(rows, cols, steps)) {
+        mb::NsSmall r{x_first, dest, scale, live, batch, rows, cols, steps, coef.data()};
+        timer.begin("ns_small", stream);
+        hipError_t e = mb::ns_small(r, stream);
+        timer.end(stream);
+        if (e != hipSuccess) return fail(MB_ERR_HIP, "Newton-Schulz launch: %s", hipGetErrorString(e));
+        return MB_OK;
+    }
     const uint16_t* in = x_first;
     for (int s = 0; s < steps; ++s) {
         const bool last = s == steps - 1;

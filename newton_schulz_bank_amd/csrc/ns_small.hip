@@ -1,0 +1,128 @@
+// Every Newton-Schulz round of a bank of small slots in one launch on gfx950.
+//
+// For slots whose Gram side m is at most 64 and whose m x n fits 4096 elements
+// (the 1 x 12 and 6 x 12 gates, for instance) the contractions are a few
+// thousand multiply-adds: one launch per contraction would be all launch cost.
+// Here one workgroup holds a slot in LDS and runs every round ("Muon Custom
+// Sizing", section 2.3; Record 7 walkthrough, section 4.2):
+//     A = RN(sig_A * X X^T),  B = RN(c*(A A) + b*A),  X' = RN(sig_X * (a*X + B X))
+// with fp32 accumulation in increasing k and one round-to-nearest-even to bf16
+// after each contraction, the same rounding points as the tiled kernels
+// (sig_A = s^2 and sig_X = s on the first round, s the slot's Frobenius scale,
+// else 1).  Tall slots are loaded transposed (X = G^T) and stored back
+// transposed.  Values stay fp32 in LDS; every stored value is a bf16 value.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace mb {
+
+namespace {
+
+constexpr int kSmallThreads = 256;
+constexpr int kSmallMaxM = 64;
+constexpr int kSmallMaxElems = 4096;
+
+struct SmallArgs {
+    const uint16_t* x0;     // input slots [batch][rows][cols], bf16 bits (unscaled)
+    uint16_t* dest;         // output slots, same layout (may equal x0)
+    const float* scale;
+    const int* live;
+    int rows, cols, m, n;
+    bool tall;
+    int steps;
+    float coef[kMaxRounds][3];
+};
+
+__device__ __forceinline__ float round_bf16(float y) { return bf16_to_f32(f32_to_bf16_rne(y)); }
+
+__global__ void __launch_bounds__(kSmallThreads) ns_small_kernel(SmallArgs p) {
+    extern __shared__ float sm[];
+    const int m = p.m, n = p.n, mn = m * n, mm = m * m;
+    float* X = sm;                 // [m][n]
+    float* Y = X + mn;             // [m][n], next round
+    float* A = Y + mn;             // [m][m]
+    float* B = A + mm;             // [m][m]
+    const int slot = blockIdx.x;
+    const int tid = threadIdx.x;
+    const uint16_t* src = p.x0 + (int64_t)slot * mn;
+    uint16_t* dst = p.dest + (int64_t)slot * mn;
+    const bool live = p.live[slot] != 0;
+    if (!live) {
+        // a zero slot's result is exactly zero (dest may alias x0: nothing was read)
+        for (int e = tid; e < mn; e += kSmallThreads) dst[e] = 0;
+        return;
+    }
+    // X[i][k] = u[i][k] (wide) or u[k][i] (tall: u is n x m)
+    for (int e = tid; e < mn; e += kSmallThreads) {
+        const int i = e / n, k = e - i * n;
+        X[e] = bf16_to_f32(p.tall ? src[(int64_t)k * m + i] : src[e]);
+    }
+    const float s = p.scale[slot];
+    __syncthreads();
+    for (int t = 0; t < p.steps; ++t) {
+        const float a = p.coef[t][0], b = p.coef[t][1], c = p.coef[t][2];
+        const float sig_a = t == 0 ? s * s : 1.f, sig_x = t == 0 ? s : 1.f;
+        for (int e = tid; e < mm; e += kSmallThreads) {
+            const int i = e / m, j = e - i * m;
+            float acc = 0.f;
+            for (int k = 0; k < n; ++k) acc = __fmaf_rn(X[i * n + k], X[j * n + k], acc);
+            A[e] = round_bf16(sig_a * acc);
+        }
+        __syncthreads();
+        for (int e = tid; e < mm; e += kSmallThreads) {
+            const int i = e / m, j = e - i * m;
+            float acc = 0.f;
+            for (int k = 0; k < m; ++k) acc = __fmaf_rn(A[i * m + k], A[k * m + j], acc);
+            B[e] = round_bf16(__fmaf_rn(b, A[e], c * acc));
+        }
+        __syncthreads();
+        for (int e = tid; e < mn; e += kSmallThreads) {
+            const int i = e / n, j = e - i * n;
+            float acc = 0.f;
+            for (int k = 0; k < m; ++k) acc = __fmaf_rn(B[i * m + k], X[k * n + j], acc);
+            Y[e] = round_bf16(sig_x * __fmaf_rn(a, X[e], acc));
+        }
+        __syncthreads();
+        float* tmp = X;
+        X = Y;
+        Y = tmp;
+    }
+    // every read of the input happened before the first barrier, so dest may alias x0
+    for (int e = tid; e < mn; e += kSmallThreads) {
+        const int i = e / n, k = e - i * n;
+        const uint16_t h = f32_to_bf16_rne(X[e]);
+        if (p.tall) dst[(int64_t)k * m + i] = h;
+        else dst[e] = h;
+    }
+}
+
+}  // namespace
+
+bool ns_small_eligible(int64_t rows, int64_t cols, int steps) {
+    const int64_t m = rows < cols ? rows : cols;
+    return steps >= 1 && steps <= kMaxRounds && m <= kSmallMaxM && rows * cols <= kSmallMaxElems;
+}
+
+hipError_t ns_small(const NsSmall& r, hipStream_t stream) {
+    SmallArgs p{};
+    p.x0 = r.x0;
+    p.dest = r.dest;
+    p.scale = r.scale;
+    p.live = r.live;
+    p.rows = (int)r.rows;
+    p.cols = (int)r.cols;
+    p.tall = r.rows > r.cols;
+    p.m = (int)(p.tall ? r.cols : r.rows);
+    p.n = (int)(p.tall ? r.rows : r.cols);
+    p.steps = r.steps;
+    for (int t = 0; t < r.steps && t < kMaxRounds; ++t) {
+        p.coef[t][0] = r.coef[t].a;
+        p.coef[t][1] = r.coef[t].b;
+        p.coef[t][2] = r.coef[t].c;
+    }
+    const size_t lds = (size_t)(2 * p.m * p.n + 2 * p.m * p.m) * sizeof(float);
+    ns_small_kernel<<<dim3((unsigned)r.batch), kSmallThreads, lds, stream>>>(p);
+    return hipGetLastError();
+}
+
+}  // namespace mb

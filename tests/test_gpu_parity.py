@@ -119,7 +119,9 @@ def test_momentum_bit_exact(shape, dtype):
 
 NS_SHAPES = [(4, 256, 256), (3, 100, 260), (3, 260, 100), (2, 130, 130), (2, 64, 512), (2, 512, 64),
              (2, 1, 12), (3, 6, 12), (2, 12, 6), (2, 768, 768), (1, 3072, 768), (1, 768, 3072), (1, 1024, 1024),
-             (1, 200, 8), (2, 257, 129)]
+             (1, 200, 8), (2, 257, 129),
+             # one workgroup per slot for every round (Gram side <= 64, <= 4096 elements)
+             (16, 1, 12), (16, 6, 12), (2, 64, 64), (3, 40, 3), (2, 16, 256), (2, 256, 16)]
 
 
 @pytest.mark.parametrize("shape", NS_SHAPES)
@@ -147,9 +149,10 @@ def test_ns_zero_slot_and_determinism():
     np.testing.assert_array_equal(y1, y2)
 
 
-def test_ns_in_place():
-    say("ns in place")
-    x = random_bf16_matrices(4, 2, 128, 192)
+@pytest.mark.parametrize("shape", [(2, 128, 192), (3, 6, 12)])
+def test_ns_in_place(shape):
+    say(f"ns in place {shape}")
+    x = random_bf16_matrices(4, *shape)
     for steps in (5, 1):
         dx = to_dev(x)
         ref = bits(api.ns_orthogonalize_batched(dx, steps=steps))
