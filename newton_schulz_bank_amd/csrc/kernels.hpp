@@ -24,10 +24,10 @@ hipError_t launch_momentum(const void* grad, void* buf, uint16_t* u, float* part
 // Per-(slot, chunk) sums of x^2 of a bf16 bank.
 hipError_t launch_sumsq(const uint16_t* x, float* partials, int64_t batch, int64_t slot_numel, bool vec,
                         hipStream_t stream);
-// scale[i] = 1 / (sqrt(sum of slot i's partials) + eps); live[i] = (sum > 0).  If sync is
-// non-null, also clears the persistent kernel's queue heads, error word and slot counters.
+// scale[i] = 1 / (sqrt(sum of slot i's partials) + eps); live[i] = (sum > 0).  Also clears, if
+// non-null, heads[0, 32) (queue heads and error word of a persistent launch) and ctr[i].
 hipError_t launch_ns_scale(const float* partials, int nchunks, int64_t batch, float eps, float* scale, int* live,
-                           int* sync, hipStream_t stream);
+                           int* heads, int* ctr, hipStream_t stream);
 // The mixed-precision apply on [batch, slot_numel].
 hipError_t launch_apply(uint16_t* w_hi, uint16_t* w_lo, const uint16_t* v, int64_t batch, int64_t slot_numel,
                         bool vec, float eta, float decay, const float* lr_mul_per_slot, hipStream_t stream);
@@ -52,10 +52,13 @@ struct NsCoef {
 };
 constexpr int kMaxRounds = 64;
 
-// Every Newton-Schulz round of a bank in one persistent launch (x0 -> ... -> dest), with xa, xb
-// as ping-pong buffers, A and Bm as scratch and sync (ns_persist_sync_ints ints, cleared by
-// launch_ns_scale) for the task queues and per-slot counters.
-struct NsPersist {
+// Every Newton-Schulz round of up to kMaxPersistBanks banks in one persistent launch: per bank
+// x0 -> ... -> dest, with xa, xb as ping-pong buffers and A, Bm as scratch; the banks' slots
+// are numbered in one sequence in the order given.  sync holds the queue heads ([0, 16)), the
+// error word ([16]) and one counter per slot ([32, 32 + total slots)), all cleared before the
+// launch (launch_ns_scale does it).
+constexpr int kMaxPersistBanks = 8;
+struct NsPersistBank {
     const uint16_t* x0;
     uint16_t* xa;
     uint16_t* xb;
@@ -64,12 +67,12 @@ struct NsPersist {
     uint16_t* Bm;
     const float* scale;
     const int* live;
-    int* sync;
     int64_t batch, rows, cols;
-    int steps;              // 1..kMaxRounds
-    const NsCoef* coef;     // host array of `steps` rounds
 };
-bool ns_persist_eligible(int64_t rows, int64_t cols, int steps);
+// Tile edge the persistent kernel uses for a slot shape (256 or 128), 0 if it cannot run it.
+int ns_persist_tile(int64_t rows, int64_t cols, int steps);
+hipError_t ns_persist(const NsPersistBank* banks, int nbanks, int tile, const NsCoef* coef, int steps, int* sync,
+                      hipStream_t stream);
 
 // Every Newton-Schulz round of a bank of small slots (Gram side <= 64, <= 4096 elements) in one
 // launch, one workgroup per slot (x0 -> dest; dest may equal x0).
@@ -84,7 +87,5 @@ struct NsSmall {
 };
 bool ns_small_eligible(int64_t rows, int64_t cols, int steps);
 hipError_t ns_small(const NsSmall& r, hipStream_t stream);
-int ns_persist_sync_ints(int64_t batch);
-hipError_t ns_persist(const NsPersist& r, hipStream_t stream);
 
 }  // namespace mb

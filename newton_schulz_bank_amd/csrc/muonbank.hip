@@ -83,45 +83,6 @@ struct Timer final : mb::RoundTimer {
 };
 
 // ---------------------------------------------------------------------------
-// side streams: a bank can be cut into slot groups that run on library-owned
-// streams, forked from and joined back to the caller's stream with events.
-// Measured on MI355X, kernels on separate streams barely overlap (average
-// concurrency 1.13 with four groups, and a slower step), so one lane is used:
-// every unit then runs on the caller's stream.
-// ---------------------------------------------------------------------------
-
-constexpr int kLanes = 1;
-
-struct DeviceStreams {
-    bool ready = false;
-    hipStream_t side[kLanes];
-    hipEvent_t fork;
-    hipEvent_t done[kLanes];
-};
-
-std::mutex g_streams_mu;
-DeviceStreams g_streams[64];
-
-// The calling thread's current device's pool, created on first use (default priority).
-hipError_t device_streams(DeviceStreams** out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    DeviceStreams& d = g_streams[dev];
-    if (!d.ready) {
-        for (int i = 0; i < kLanes; ++i) {
-            if ((e = hipStreamCreateWithFlags(&d.side[i], hipStreamNonBlocking)) != hipSuccess) return e;
-            if ((e = hipEventCreateWithFlags(&d.done[i], hipEventDisableTiming)) != hipSuccess) return e;
-        }
-        if ((e = hipEventCreateWithFlags(&d.fork, hipEventDisableTiming)) != hipSuccess) return e;
-        d.ready = true;
-    }
-    *out = &d;
-    return hipSuccess;
-}
-
-// ---------------------------------------------------------------------------
 // validation helpers
 // ---------------------------------------------------------------------------
 
@@ -186,7 +147,7 @@ mb_status check_hparams(const mb_hparams& hp) {
 size_t round_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // Workspace of one bank: u, two ping-pong X buffers, A, B, partial sums, scale, live, and the
-// persistent kernel's queue heads and slot counters (32 ints per slot group + one per slot).
+// persistent kernel's queue heads, error word and slot counters (32 ints + one per slot).
 struct BankWs {
     size_t u, x1, x2, A, Bm, partials, scale, live, sync, total;
 };
@@ -205,12 +166,56 @@ BankWs bank_ws_layout(int64_t batch, int64_t rows, int64_t cols, bool vec) {
     w.partials = off; off += round_up((size_t)batch * mb::stream_chunks(rows * cols, vec) * 4);
     w.scale = off; off += round_up((size_t)batch * 4);
     w.live = off; off += round_up((size_t)batch * 4);
-    w.sync = off; off += round_up((size_t)(32 * kLanes + batch) * 4);
+    w.sync = off; off += round_up((size_t)(32 + batch) * 4);
     w.total = off;
     return w;
 }
 
 float f32(double v) { return (float)v; }
+
+// The persistent launches of one muon_bank_step: banks whose slots the persistent kernel can run,
+// grouped by tile edge, in chunks of at most kMaxPersistBanks banks.  Each chunk has its own
+// sync block (queue heads and error word, then one counter per slot of the chunk) in the step's
+// trailing sync region.
+struct PersistChunk {
+    int tile;
+    std::vector<int32_t> banks;
+    size_t sync_off;        // ints from the start of the sync region
+    std::vector<int> base;  // number of each bank's first slot within the chunk
+};
+
+struct StepPlan {
+    std::vector<PersistChunk> chunks;
+    std::vector<int> chunk_of;     // per bank: its chunk, or -1
+    size_t sync_ints = 0;
+};
+
+StepPlan plan_step(const mb_bank* banks, int32_t num_banks) {
+    StepPlan pl;
+    pl.chunk_of.assign((size_t)num_banks, -1);
+    for (int tile : {256, 128}) {
+        PersistChunk cur{tile, {}, 0, {}};
+        int slots = 0;
+        auto flush = [&]() {
+            if (cur.banks.empty()) return;
+            cur.sync_off = pl.sync_ints;
+            pl.sync_ints += 32 + (size_t)slots;
+            for (int32_t bi : cur.banks) pl.chunk_of[(size_t)bi] = (int)pl.chunks.size();
+            pl.chunks.push_back(cur);
+            cur = PersistChunk{tile, {}, 0, {}};
+            slots = 0;
+        };
+        for (int32_t i = 0; i < num_banks; ++i) {
+            if (mb::ns_persist_tile(banks[i].rows, banks[i].cols, 1) != tile) continue;
+            cur.base.push_back(slots);
+            cur.banks.push_back(i);
+            slots += (int)banks[i].batch;
+            if ((int)cur.banks.size() == mb::kMaxPersistBanks) flush();
+        }
+        flush();
+    }
+    return pl;
+}
 
 // 0: every round of a bank in one persistent launch where the shape allows it; 1: one launch per
 // contraction.
@@ -233,10 +238,11 @@ mb_status run_ns(const uint16_t* x_first, uint16_t* dest, uint16_t* x1, uint16_t
                  int64_t batch, int64_t rows, int64_t cols, const std::vector<mb::NsCoef>& coef,
                  const float* scale, const int* live, int* sync, hipStream_t stream, Timer& timer) {
     const int steps = (int)coef.size();
-    if (g_ns_path.load() == 0 && mb::ns_persist_eligible(rows, cols, steps)) {
-        mb::NsPersist r{x_first, x1, x2, dest, A, Bm, scale, live, sync, batch, rows, cols, steps, coef.data()};
+    const int tile = mb::ns_persist_tile(rows, cols, steps);
+    if (g_ns_path.load() == 0 && tile != 0 && sync) {
+        const mb::NsPersistBank r{x_first, x1, x2, dest, A, Bm, scale, live, batch, rows, cols};
         timer.begin("ns_persist", stream);
-        hipError_t e = mb::ns_persist(r, stream);
+        hipError_t e = mb::ns_persist(&r, 1, tile, coef.data(), steps, sync, stream);
         timer.end(stream);
         if (e != hipSuccess) return fail(MB_ERR_HIP, "Newton-Schulz launch: %s", hipGetErrorString(e));
         return MB_OK;
@@ -312,6 +318,7 @@ size_t mb_step_workspace_bytes(const mb_bank* banks, int32_t num_banks) {
         if (check_shape(b.batch, b.rows, b.cols, "mb_step_workspace_bytes") != MB_OK) return 0;
         total += bank_ws_layout(b.batch, b.rows, b.cols, (b.rows * b.cols) % 8 == 0).total;
     }
+    total += round_up(plan_step(banks, num_banks).sync_ints * 4);
     return total;
 }
 
@@ -387,7 +394,8 @@ mb_status ns_orthogonalize_impl(const uint16_t* x, uint16_t* y, int64_t batch, i
     if (e != hipSuccess) return fail(MB_ERR_HIP, "sumsq launch: %s", hipGetErrorString(e));
     timer.begin("ns_scale", st);
     int* sync = (int*)(ws + L.sync);
-    e = mb::launch_ns_scale(partials, mb::stream_chunks(rows * cols, vec), batch, f32(eps), scale, live, sync, st);
+    e = mb::launch_ns_scale(partials, mb::stream_chunks(rows * cols, vec), batch, f32(eps), scale, live, sync, sync + 32,
+                            st);
     timer.end(st);
     if (e != hipSuccess) return fail(MB_ERR_HIP, "ns_scale launch: %s", hipGetErrorString(e));
     // in place with a single round: write the round to scratch, then copy
@@ -483,6 +491,9 @@ mb_status muon_bank_step(const mb_bank* banks, int32_t num_banks, const mb_hpara
             ranges.push_back({(uintptr_t)b.lr_mul_per_slot, (uintptr_t)b.lr_mul_per_slot + b.batch * 4, "lr_mul_per_slot"});
         need += bank_ws_layout(b.batch, b.rows, b.cols, (b.rows * b.cols) % 8 == 0).total;
     }
+    const StepPlan plan = plan_step(banks, num_banks);
+    const size_t banks_bytes = need;
+    need += round_up(plan.sync_ints * 4);
     if (!workspace || workspace_bytes < need)
         return fail(MB_ERR_WORKSPACE, "muon_bank_step: workspace of %zu bytes needed, %zu given", need,
                     workspace ? workspace_bytes : (size_t)0);
@@ -491,104 +502,109 @@ mb_status muon_bank_step(const mb_bank* banks, int32_t num_banks, const mb_hpara
     s = check_no_overlap(ranges);
     if (s != MB_OK) return s;
 
-    // ---- enqueue: every bank is cut into up to kLanes contiguous slot groups (small banks stay
-    // whole); group g of the call runs on side stream g % kLanes
+    // ---- enqueue, all on the caller's stream: momentum and scale of every bank, the persistent
+    // Newton-Schulz launches (each over several banks), the other banks' Newton-Schulz rounds,
+    // then every apply
     hipStream_t st = (hipStream_t)stream;
-    struct Unit {
-        int32_t bank;
-        int64_t s0, s1;
-        int32_t group;
-    };
-    std::vector<Unit> units;
-    for (int32_t i = 0; i < num_banks; ++i) {
-        const mb_bank& b = banks[i];
-        const bool big = b.rows * b.cols >= 65536 && b.batch >= 2 * kLanes;
-        const int64_t groups = big ? kLanes : 1;
-        for (int64_t g = 0; g < groups; ++g)
-            units.push_back({i, b.batch * g / groups, b.batch * (g + 1) / groups, (int32_t)g});
-    }
-    std::lock_guard<std::mutex> lk(g_streams_mu);
-    DeviceStreams* ds = nullptr;
-    const bool fork = units.size() > 1;
-    if (fork) {
-        hipError_t e = device_streams(&ds);
-        if (e != hipSuccess) return fail(MB_ERR_HIP, "side streams: %s", hipGetErrorString(e));
-        if ((e = hipEventRecord(ds->fork, st)) != hipSuccess) return fail(MB_ERR_HIP, "fork: %s", hipGetErrorString(e));
-        for (int l = 0; l < kLanes; ++l)
-            if ((e = hipStreamWaitEvent(ds->side[l], ds->fork, 0)) != hipSuccess)
-                return fail(MB_ERR_HIP, "fork: %s", hipGetErrorString(e));
-    }
     Timer timer;
     char* ws = (char*)workspace;
-    std::vector<size_t> bank_off(num_banks);
-    {
-        size_t off = 0;
-        for (int32_t i = 0; i < num_banks; ++i) {
-            bank_off[i] = off;
-            off += bank_ws_layout(banks[i].batch, banks[i].rows, banks[i].cols, (banks[i].rows * banks[i].cols) % 8 == 0).total;
+    int* sync = (int*)(ws + banks_bytes);
+    const std::vector<mb::NsCoef> coef = ns_coefs(hp.ns_steps, hp.a, hp.b, hp.c, hp.ns_schedule);
+    const bool persist = g_ns_path.load() == 0;
+    struct Run {
+        int64_t slot;
+        bool vec;
+        int nch;
+        uint16_t *u, *v, *x1, *x2, *A, *Bm, *dest;
+        float *partials, *scale;
+        int* live;
+    };
+    std::vector<Run> runs((size_t)num_banks);
+    size_t off = 0;
+    for (int32_t i = 0; i < num_banks; ++i) {
+        const mb_bank& b = banks[i];
+        Run& r = runs[(size_t)i];
+        r.slot = b.rows * b.cols;
+        r.vec = r.slot % 8 == 0;
+        r.nch = mb::stream_chunks(r.slot, r.vec);
+        const BankWs L = bank_ws_layout(b.batch, b.rows, b.cols, r.vec);
+        char* bw = ws + off;
+        off += L.total;
+        r.u = b.u_out ? b.u_out : (uint16_t*)(bw + L.u);
+        r.v = b.v_out ? b.v_out : (uint16_t*)(bw + L.u);    // u is dead once round 1 read it
+        r.x1 = (uint16_t*)(bw + L.x1);
+        r.x2 = (uint16_t*)(bw + L.x2);
+        r.A = (uint16_t*)(bw + L.A);
+        r.Bm = (uint16_t*)(bw + L.Bm);
+        r.partials = (float*)(bw + L.partials);
+        r.scale = (float*)(bw + L.scale);
+        r.live = (int*)(bw + L.live);
+        // with one round and no v_out, the round would read u while writing v in the same buffer
+        r.dest = (hp.ns_steps == 1 && r.v == r.u) ? r.x2 : r.v;
+    }
+    const float mu = f32(hp.momentum);
+    const float nu = f32(1.0 - hp.momentum);
+    for (int32_t i = 0; i < num_banks; ++i) {
+        const mb_bank& b = banks[i];
+        const Run& r = runs[(size_t)i];
+        timer.begin("momentum", st);
+        hipError_t e = mb::launch_momentum(b.grad, b.momentum, r.u, r.partials, b.batch, r.slot,
+                                           b.grad_dtype == MB_F32, r.vec, mu, nu, st);
+        timer.end(st);
+        if (e != hipSuccess) return fail(MB_ERR_HIP, "momentum launch: %s", hipGetErrorString(e));
+        // a bank in a persistent launch clears its slot counters; the chunk's first bank clears
+        // the chunk's queue heads and error word
+        int *heads = nullptr, *ctr = nullptr;
+        const int ch = plan.chunk_of[(size_t)i];
+        if (persist && ch >= 0) {
+            const PersistChunk& c = plan.chunks[(size_t)ch];
+            int* cs = sync + c.sync_off;
+            size_t k = 0;
+            while (c.banks[k] != i) ++k;
+            if (k == 0) heads = cs;
+            ctr = cs + 32 + c.base[k];
+        }
+        timer.begin("ns_scale", st);
+        e = mb::launch_ns_scale(r.partials, r.nch, b.batch, f32(hp.eps), r.scale, r.live, heads, ctr, st);
+        timer.end(st);
+        if (e != hipSuccess) return fail(MB_ERR_HIP, "ns_scale launch: %s", hipGetErrorString(e));
+    }
+    if (persist) {
+        for (const PersistChunk& c : plan.chunks) {
+            std::vector<mb::NsPersistBank> pb;
+            for (int32_t i : c.banks) {
+                const mb_bank& b = banks[i];
+                const Run& r = runs[(size_t)i];
+                pb.push_back({r.u, r.x1, r.x2, r.dest, r.A, r.Bm, r.scale, r.live, b.batch, b.rows, b.cols});
+            }
+            timer.begin("ns_persist", st);
+            hipError_t e = mb::ns_persist(pb.data(), (int)pb.size(), c.tile, coef.data(), hp.ns_steps,
+                                          sync + c.sync_off, st);
+            timer.end(st);
+            if (e != hipSuccess) return fail(MB_ERR_HIP, "Newton-Schulz launch: %s", hipGetErrorString(e));
         }
     }
-    for (size_t ui = 0; ui < units.size(); ++ui) {
-        const Unit& un = units[ui];
-        const mb_bank& b = banks[un.bank];
-        hipStream_t us = fork ? ds->side[ui % kLanes] : st;
-        const int64_t slot = b.rows * b.cols;
-        const int64_t m = b.rows < b.cols ? b.rows : b.cols;
-        const bool vec = slot % 8 == 0;
-        const int nch = mb::stream_chunks(slot, vec);
-        const BankWs L = bank_ws_layout(b.batch, b.rows, b.cols, vec);
-        char* bw = ws + bank_off[un.bank];
-        const int64_t s0 = un.s0, nb = un.s1 - un.s0;
+    for (int32_t i = 0; i < num_banks; ++i) {
+        if (persist && plan.chunk_of[(size_t)i] >= 0) continue;
+        const mb_bank& b = banks[i];
+        const Run& r = runs[(size_t)i];
+        s = run_ns(r.u, r.dest, r.x1, r.x2, r.A, r.Bm, b.batch, b.rows, b.cols, coef, r.scale, r.live, nullptr, st,
+                   timer);
+        if (s != MB_OK) return s;
+    }
+    for (int32_t i = 0; i < num_banks; ++i) {
+        const mb_bank& b = banks[i];
+        const Run& r = runs[(size_t)i];
         // host scalars in double, rounded once to float32
-        const float mu = f32(hp.momentum);
-        const float nu = f32(1.0 - hp.momentum);
         const float decay = f32(1.0 - hp.lr * hp.weight_decay * b.wd_mul);
         const float eta = f32(hp.lr * std::sqrt(std::max(1.0, (double)b.rows / (double)b.cols)) * b.lr_mul);
-
-        const size_t gsz = b.grad_dtype == MB_F32 ? 4 : 2;
-        const void* grad = (const char*)b.grad + s0 * slot * gsz;
-        void* mom = (char*)b.momentum + s0 * slot * gsz;
-        uint16_t* w_hi = b.w_hi + s0 * slot;
-        uint16_t* w_lo = b.w_lo + s0 * slot;
-        const float* lrm = b.lr_mul_per_slot ? b.lr_mul_per_slot + s0 : nullptr;
-        uint16_t* u = (b.u_out ? b.u_out : (uint16_t*)(bw + L.u)) + s0 * slot;
-        uint16_t* v = (b.v_out ? b.v_out : (uint16_t*)(bw + L.u)) + s0 * slot;   // u is dead once round 1 read it
-        uint16_t* x1 = (uint16_t*)(bw + L.x1) + s0 * slot;
-        uint16_t* x2 = (uint16_t*)(bw + L.x2) + s0 * slot;
-        uint16_t* A = (uint16_t*)(bw + L.A) + s0 * m * m;
-        uint16_t* Bm = (uint16_t*)(bw + L.Bm) + s0 * m * m;
-        float* partials = (float*)(bw + L.partials) + s0 * nch;
-        float* scale = (float*)(bw + L.scale) + s0;
-        int* live = (int*)(bw + L.live) + s0;
-        int* sync = (int*)(bw + L.sync) + 32 * un.group + s0;
-
-        timer.begin("momentum", us);
-        hipError_t e = mb::launch_momentum(grad, mom, u, partials, nb, slot, b.grad_dtype == MB_F32, vec, mu, nu, us);
-        timer.end(us);
-        if (e != hipSuccess) return fail(MB_ERR_HIP, "momentum launch: %s", hipGetErrorString(e));
-        timer.begin("ns_scale", us);
-        e = mb::launch_ns_scale(partials, nch, nb, f32(hp.eps), scale, live, sync, us);
-        timer.end(us);
-        if (e != hipSuccess) return fail(MB_ERR_HIP, "ns_scale launch: %s", hipGetErrorString(e));
-        // with one round and no v_out, the round would read u while writing v in the same buffer
-        uint16_t* dest = (hp.ns_steps == 1 && v == u) ? x2 : v;
-        s = run_ns(u, dest, x1, x2, A, Bm, nb, b.rows, b.cols, ns_coefs(hp.ns_steps, hp.a, hp.b, hp.c, hp.ns_schedule),
-                   scale, live, sync, us, timer);
-        if (s != MB_OK) return s;
-        timer.begin("apply", us);
-        e = mb::launch_apply(w_hi, w_lo, dest, nb, slot, vec, eta, decay, lrm, us);
-        timer.end(us);
+        timer.begin("apply", st);
+        hipError_t e = mb::launch_apply(b.w_hi, b.w_lo, r.dest, b.batch, r.slot, r.vec, eta, decay, b.lr_mul_per_slot, st);
+        timer.end(st);
         if (e != hipSuccess) return fail(MB_ERR_HIP, "apply launch: %s", hipGetErrorString(e));
-        if (dest != v) {
-            e = hipMemcpyAsync(v, dest, (size_t)(nb * slot) * 2, hipMemcpyDeviceToDevice, us);
+        if (r.dest != r.v) {
+            e = hipMemcpyAsync(r.v, r.dest, (size_t)(b.batch * r.slot) * 2, hipMemcpyDeviceToDevice, st);
             if (e != hipSuccess) return fail(MB_ERR_HIP, "copy: %s", hipGetErrorString(e));
-        }
-    }
-    if (fork) {
-        for (int l = 0; l < kLanes; ++l) {
-            hipError_t e = hipEventRecord(ds->done[l], ds->side[l]);
-            if (e == hipSuccess) e = hipStreamWaitEvent(st, ds->done[l], 0);
-            if (e != hipSuccess) return fail(MB_ERR_HIP, "join: %s", hipGetErrorString(e));
         }
     }
     return ok();

@@ -1,4 +1,4 @@
-// All Newton-Schulz rounds of a bank in one persistent launch on gfx950.
+// All Newton-Schulz rounds of one or more banks in one persistent launch on gfx950.
 //
 // The rounds ("Muon Custom Sizing", section 2.3; Record 7 walkthrough, section
 // 4.2) chain three contractions per slot and round,
@@ -6,17 +6,19 @@
 //     A = G^T G,   B as above,        G' = a*G + G B      (tall G),
 // and the slots are independent.  Instead of one launch per contraction (whose
 // last wave of tiles leaves most CUs idle and whose boundary writes back the
-// whole L2), every 256x256 output tile of every contraction is a task, and the
-// workgroups of one launch take tasks from a queue while they last.
+// whole L2), every 256x256 output tile of every contraction of every bank is a
+// task, and the workgroups of one launch take tasks from a queue while they
+// last: the short contractions of one bank fill the gaps of another's.
 //
 // Placement.  Workgroups are spread over the XCDs, each with its own L2, and
-// the L2s are not coherent with each other inside a kernel.  Slot s belongs to
-// XCD s % nq: its tasks sit in that XCD's queue, and only workgroups running on
-// that XCD (read from the XCC_ID hardware register) take them, so a slot's
-// intermediate results are produced and consumed through one L2.
+// the L2s are not coherent with each other inside a kernel.  The slots of all
+// banks are numbered in one sequence; slot g belongs to XCD g % nq: its tasks
+// sit in that XCD's queue, and only workgroups running on that XCD (read from
+// the XCC_ID hardware register) take them, so a slot's intermediate results
+// are produced and consumed through one L2.
 //
 // Ordering.  A queue lists the tasks round by round, contraction by
-// contraction, slot by slot.  A task needs every tile of the previous
+// contraction, bank by bank, slot by slot.  A task needs every tile of the previous
 // contraction of its slot: its slot's counter of finished tasks must have
 // reached the number of tasks that come before it in that slot's chain.  A
 // producer waits until its stores are acknowledged (they are then in the L2),
@@ -37,8 +39,9 @@ namespace {
 
 constexpr uint64_t kWaitCapTicks = 20000000;   // 200 ms of the 100 MHz constant clock
 constexpr int kXccIdReg = 20 | (0 << 6) | (15 << 11);   // hwreg(HW_REG_XCC_ID, 0, 16)
+constexpr int kMaxQueues = 16;
 
-struct PersistArgs {
+struct PersistBank {
     const uint16_t* x0;     // round input of round 0 (unscaled)
     uint16_t* xa;           // outputs of rounds 0, 2, 4, ... (except the last)
     uint16_t* xb;           // outputs of rounds 1, 3, 5, ...
@@ -47,12 +50,25 @@ struct PersistArgs {
     uint16_t* Bm;
     const float* scale;
     const int* live;
-    int* sync;              // [0, 16) queue heads, [16] error word, [32, 32 + batch) per-slot counters
     int64_t slot;           // elements per slot of X
     int64_t mm;             // elements per slot of A, B
     int m, n;               // Gram size and long side (m <= n)
     int tm, tn;             // tiles along m and along n
-    int batch, steps, nq;
+    int batch;
+    int base;               // number of the bank's first slot in the launch's slot sequence
+    int tall;
+};
+
+struct PersistArgs {
+    PersistBank bank[kMaxPersistBanks];
+    int nbanks, steps, nq;
+    int* heads;             // [nq] next task of each queue
+    int* err;               // set when a dependency wait hits its time cap
+    int* ctr;               // [total slots] tasks finished per slot
+    // per queue: tasks of one round, of its Gram block and of its polynomial block, and the
+    // number of slots of each bank on the queue
+    int per_round[kMaxQueues], blk_g[kMaxQueues], blk_p[kMaxQueues];
+    int ls[kMaxQueues][kMaxPersistBanks];
     float coef[kMaxRounds][3];   // (a, b, c) of each round
 };
 
@@ -60,21 +76,17 @@ __device__ __forceinline__ int ld_relaxed(const int* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <bool TALL, class C>
+__host__ __device__ __forceinline__ int sym_count(int tm) { return tm * (tm + 1) / 2; }
+
+template <class C>
 __global__ void __launch_bounds__(C::NT, 2) ns_persist_kernel(PersistArgs p) {
     static_assert(C::BM == C::BN, "square tiles");
     constexpr int kTile = C::BM;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[C::RING];
     __shared__ int s_task;
-    int* heads = p.sync;
-    int* err = p.sync + 16;
-    int* ctr = p.sync + 32;
     const int tid = threadIdx.x;
     const int q = (int)(__builtin_amdgcn_s_getreg(kXccIdReg) & 0xFFFF) % p.nq;
-    const int ls = q < p.batch ? (p.batch - q + p.nq - 1) / p.nq : 0;    // slots q, q + nq, ...
-    const int nG = p.tm * (p.tm + 1) / 2, nP = nG, nU = p.tm * p.tn;
-    const int chain = nG + nP + nU;                                       // tasks per slot and round
-    const int per_round = ls * chain;
+    const int per_round = p.per_round[q];
     const int total = p.steps * per_round;
 
     // Every branch in this loop is wave-uniform: the queue and counter traffic is done by all
@@ -85,29 +97,44 @@ __global__ void __launch_bounds__(C::NT, 2) ns_persist_kernel(PersistArgs p) {
     const bool leader = __builtin_amdgcn_readfirstlane(tid >> 6) == 0;
     const int one = (tid & 63) == 0 ? 1 : 0;
     if (leader) {
-        const int got = __hip_atomic_fetch_add(heads + q, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int got = __hip_atomic_fetch_add(p.heads + q, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_task = __builtin_amdgcn_readfirstlane(got);
     }
     __syncthreads();
     int idx = __builtin_amdgcn_readfirstlane(s_task);
     while (idx >= 0 && idx < total) {
+        // ---- decode: round t, contraction (phase), bank, slot, tile
         const int t = idx / per_round;
         int r = idx - t * per_round;
-        int phase, l, tile;
-        if (r < ls * nG) { phase = 0; l = r / nG; tile = r - l * nG; }
-        else if ((r -= ls * nG) < ls * nP) { phase = 1; l = r / nP; tile = r - l * nP; }
-        else { r -= ls * nP; phase = 2; l = r / nU; tile = r - l * nU; }
-        const int slot = q + l * p.nq;
-        const int need = t * chain + (phase == 0 ? 0 : phase == 1 ? nG : nG + nP);
+        int phase;
+        if (r < p.blk_g[q]) phase = 0;
+        else if ((r -= p.blk_g[q]) < p.blk_p[q]) phase = 1;
+        else { r -= p.blk_p[q]; phase = 2; }
+        int b = 0, ntile = 1;
+        for (; b < p.nbanks - 1; ++b) {
+            ntile = phase == 2 ? p.bank[b].tm * p.bank[b].tn : sym_count(p.bank[b].tm);
+            const int cnt = p.ls[q][b] * ntile;
+            if (r < cnt) break;
+            r -= cnt;
+        }
+        const PersistBank& bk = p.bank[b];
+        ntile = phase == 2 ? bk.tm * bk.tn : sym_count(bk.tm);
+        const int l = r / ntile, tile = r - l * ntile;
+        const int first = ((q - bk.base) % p.nq + p.nq) % p.nq;      // the bank's first slot on this queue
+        const int slot = first + l * p.nq;
+        int* ctr = p.ctr + bk.base + slot;
+        const int nG = sym_count(bk.tm);
+        const int chain = 2 * nG + bk.tm * bk.tn;                      // tasks per slot and round
+        const int need = t * chain + (phase == 0 ? 0 : phase == 1 ? nG : 2 * nG);
 
-        if (leader && need > 0 && __builtin_amdgcn_readfirstlane(ld_relaxed(ctr + slot)) < need) {
+        if (leader && need > 0 && __builtin_amdgcn_readfirstlane(ld_relaxed(ctr)) < need) {
             const uint64_t t0 = wall_clock64();
             for (int spin = 0;; ++spin) {
                 __builtin_amdgcn_s_sleep(2);
-                if (__builtin_amdgcn_readfirstlane(ld_relaxed(ctr + slot)) >= need) break;
-                if ((spin & 63) == 63 && (__builtin_amdgcn_readfirstlane(ld_relaxed(err)) != 0 ||
+                if (__builtin_amdgcn_readfirstlane(ld_relaxed(ctr)) >= need) break;
+                if ((spin & 63) == 63 && (__builtin_amdgcn_readfirstlane(ld_relaxed(p.err)) != 0 ||
                                           wall_clock64() - t0 > kWaitCapTicks)) {
-                    __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(p.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     break;
                 }
             }
@@ -116,14 +143,15 @@ __global__ void __launch_bounds__(C::NT, 2) ns_persist_kernel(PersistArgs p) {
         int ltid = tid;
         asm volatile("" : "+v"(ltid));
 
+        const bool tall = bk.tall != 0;
         const bool last = t == p.steps - 1;
-        const uint16_t* xin = t == 0 ? p.x0 : ((t & 1) ? p.xa : p.xb);
-        uint16_t* xout = last ? p.dest : ((t & 1) ? p.xb : p.xa);
-        const uint16_t* xs = xin + (int64_t)slot * p.slot;
-        uint16_t* As = p.A + (int64_t)slot * p.mm;
-        uint16_t* Bs = p.Bm + (int64_t)slot * p.mm;
-        const bool live = p.live[slot] != 0;
-        const uint32_t xbytes = (uint32_t)(p.slot * 2), abytes = (uint32_t)(p.mm * 2);
+        const uint16_t* xin = t == 0 ? bk.x0 : ((t & 1) ? bk.xa : bk.xb);
+        uint16_t* xout = last ? bk.dest : ((t & 1) ? bk.xb : bk.xa);
+        const uint16_t* xs = xin + (int64_t)slot * bk.slot;
+        uint16_t* As = bk.A + (int64_t)slot * bk.mm;
+        uint16_t* Bs = bk.Bm + (int64_t)slot * bk.mm;
+        const bool live = bk.live[slot] != 0;
+        const uint32_t xbytes = (uint32_t)(bk.slot * 2), abytes = (uint32_t)(bk.mm * 2);
 
         TileJob jb;
         jb.alpha = 1.f;
@@ -132,33 +160,34 @@ __global__ void __launch_bounds__(C::NT, 2) ns_persist_kernel(PersistArgs p) {
         if (phase == 0) {
             if (live) {
                 int ti, tj;
-                sym_tile(tile, p.tm, ti, tj);
+                sym_tile(tile, bk.tm, ti, tj);
                 jb.P = make_rsrc(xs, xbytes);
                 jb.Q = jb.P;
                 jb.X = jb.P;
-                jb.ldp = jb.ldq = TALL ? p.m : p.n;
+                jb.ldp = jb.ldq = tall ? bk.m : bk.n;
                 jb.ldx = jb.ldp;
-                jb.ldo = p.m;
-                jb.K = p.n;
+                jb.ldo = bk.m;
+                jb.K = bk.n;
                 jb.i0 = ti * kTile;
                 jb.j0 = tj * kTile;
                 jb.out = As;
                 jb.mirror = ti != tj;
                 if (t == 0) {
-                    const float s = p.scale[slot];
-                    jb.sig = s * s;
+                    const float sc = bk.scale[slot];
+                    jb.sig = sc * sc;
                 }
-                gemm_tile<!TALL, !TALL, EPI_GRAM, C, POL_SC1>(jb, smem, ltid);
+                if (tall) gemm_tile<false, false, EPI_GRAM, C, POL_SC1>(jb, smem, ltid);
+                else gemm_tile<true, true, EPI_GRAM, C, POL_SC1>(jb, smem, ltid);
             }
         } else if (phase == 1) {
             if (live) {
                 int ti, tj;
-                sym_tile(tile, p.tm, ti, tj);
+                sym_tile(tile, bk.tm, ti, tj);
                 jb.P = make_rsrc(As, abytes);
                 jb.Q = jb.P;
                 jb.X = jb.P;
-                jb.ldp = jb.ldq = jb.ldx = jb.ldo = p.m;
-                jb.K = p.m;
+                jb.ldp = jb.ldq = jb.ldx = jb.ldo = bk.m;
+                jb.K = bk.m;
                 jb.i0 = ti * kTile;
                 jb.j0 = tj * kTile;
                 jb.out = Bs;
@@ -169,27 +198,28 @@ __global__ void __launch_bounds__(C::NT, 2) ns_persist_kernel(PersistArgs p) {
             }
         } else {
             // wide: X' (m x n) = a*X + B X;  tall: G' (n x m) = a*G + G B
-            const int nt_cols = TALL ? p.tm : p.tn;
+            const int nt_cols = tall ? bk.tm : bk.tn;
             const int ti = tile / nt_cols, tj = tile - ti * nt_cols;
-            const int ld = TALL ? p.m : p.n;
-            uint16_t* os = xout + (int64_t)slot * p.slot;
+            const int ld = tall ? bk.m : bk.n;
+            uint16_t* os = xout + (int64_t)slot * bk.slot;
             if (live) {
                 const i32x4 rx = make_rsrc(xs, xbytes);
                 const i32x4 rb = make_rsrc(Bs, abytes);
-                jb.P = TALL ? rx : rb;
-                jb.Q = TALL ? rb : rx;
+                jb.P = tall ? rx : rb;
+                jb.Q = tall ? rb : rx;
                 jb.X = rx;
-                jb.ldp = p.m;
-                jb.ldq = TALL ? p.m : p.n;
+                jb.ldp = bk.m;
+                jb.ldq = tall ? bk.m : bk.n;
                 jb.ldx = jb.ldo = ld;
-                jb.K = p.m;
+                jb.K = bk.m;
                 jb.i0 = ti * kTile;
                 jb.j0 = tj * kTile;
                 jb.out = os;
                 jb.mirror = false;
                 jb.beta = p.coef[t][0];
-                if (t == 0) jb.sig = p.scale[slot];
-                gemm_tile<true, TALL, EPI_UPDATE, C, POL_SC1>(jb, smem, ltid);
+                if (t == 0) jb.sig = bk.scale[slot];
+                if (tall) gemm_tile<true, true, EPI_UPDATE, C, POL_SC1>(jb, smem, ltid);
+                else gemm_tile<true, false, EPI_UPDATE, C, POL_SC1>(jb, smem, ltid);
             } else if (last) {
                 // a zero slot's result is exactly zero
                 const int i0 = ti * kTile, j0 = tj * kTile;
@@ -206,9 +236,9 @@ __global__ void __launch_bounds__(C::NT, 2) ns_persist_kernel(PersistArgs p) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (leader) {
-            __hip_atomic_fetch_add(ctr + slot, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(ctr, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             s_task = __builtin_amdgcn_readfirstlane(
-                __hip_atomic_fetch_add(heads + q, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                __hip_atomic_fetch_add(p.heads + q, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
         }
         __syncthreads();
         idx = __builtin_amdgcn_readfirstlane(s_task);
@@ -229,7 +259,7 @@ hipError_t device_shape(DeviceShape* out) {
         DeviceShape d;
         if ((e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
         if ((e = hipDeviceGetAttribute(&d.xccs, hipDeviceAttributeNumberOfXccs, dev)) != hipSuccess) return e;
-        if (d.xccs < 1 || d.xccs > 16 || d.cus % d.xccs != 0) d.xccs = 1;
+        if (d.xccs < 1 || d.xccs > kMaxQueues || d.cus % d.xccs != 0) d.xccs = 1;
         cached = d;
         cached_dev = dev;
     }
@@ -237,62 +267,79 @@ hipError_t device_shape(DeviceShape* out) {
     return hipSuccess;
 }
 
-// Tile edge of the persistent kernel for a slot of m x n (m <= n), 0 if it cannot run it.
-int persist_tile(int64_t m, int64_t n) {
+}  // namespace
+
+int ns_persist_tile(int64_t rows, int64_t cols, int steps) {
+    const int64_t m = rows < cols ? rows : cols, n = rows < cols ? cols : rows;
+    if (steps < 1 || steps > kMaxRounds || m * n > ((int64_t)1 << 30) || m * m > ((int64_t)1 << 30)) return 0;
     if (m % 256 == 0 && n % 256 == 0) return 256;
     if (m % 128 == 0 && n % 128 == 0) return 128;
     return 0;
 }
 
-}  // namespace
-
-bool ns_persist_eligible(int64_t rows, int64_t cols, int steps) {
-    const int64_t m = rows < cols ? rows : cols, n = rows < cols ? cols : rows;
-    return steps >= 1 && steps <= kMaxRounds && persist_tile(m, n) != 0 && m * n <= ((int64_t)1 << 30) && m * m <= ((int64_t)1 << 30);
-}
-
-int ns_persist_sync_ints(int64_t batch) { return 32 + (int)batch; }
-
-hipError_t ns_persist(const NsPersist& r, hipStream_t stream) {
+hipError_t ns_persist(const NsPersistBank* banks, int nbanks, int tile, const NsCoef* coef, int steps, int* sync,
+                      hipStream_t stream) {
+    if (nbanks < 1 || nbanks > kMaxPersistBanks || (tile != 256 && tile != 128) || steps < 1 || steps > kMaxRounds)
+        return hipErrorInvalidValue;
     DeviceShape d;
     hipError_t e = device_shape(&d);
     if (e != hipSuccess) return e;
-    const bool tall = r.rows > r.cols;
     PersistArgs p{};
-    p.x0 = r.x0;
-    p.xa = r.xa;
-    p.xb = r.xb;
-    p.dest = r.dest;
-    p.A = r.A;
-    p.Bm = r.Bm;
-    p.scale = r.scale;
-    p.live = r.live;
-    p.sync = r.sync;
-    p.slot = r.rows * r.cols;
-    p.m = (int)(tall ? r.cols : r.rows);
-    p.n = (int)(tall ? r.rows : r.cols);
-    p.mm = (int64_t)p.m * p.m;
-    const int tile = persist_tile(p.m, p.n);
-    p.tm = p.m / tile;
-    p.tn = p.n / tile;
-    p.batch = (int)r.batch;
-    p.steps = r.steps;
+    p.nbanks = nbanks;
+    p.steps = steps;
     p.nq = d.xccs;
-    for (int t = 0; t < r.steps && t < kMaxRounds; ++t) {
-        p.coef[t][0] = r.coef[t].a;
-        p.coef[t][1] = r.coef[t].b;
-        p.coef[t][2] = r.coef[t].c;
+    p.heads = sync;
+    p.err = sync + 16;
+    p.ctr = sync + 32;
+    int base = 0;
+    for (int b = 0; b < nbanks; ++b) {
+        const NsPersistBank& r = banks[b];
+        PersistBank& k = p.bank[b];
+        k.tall = r.rows > r.cols ? 1 : 0;
+        k.x0 = r.x0;
+        k.xa = r.xa;
+        k.xb = r.xb;
+        k.dest = r.dest;
+        k.A = r.A;
+        k.Bm = r.Bm;
+        k.scale = r.scale;
+        k.live = r.live;
+        k.slot = r.rows * r.cols;
+        k.m = (int)(k.tall ? r.cols : r.rows);
+        k.n = (int)(k.tall ? r.rows : r.cols);
+        k.mm = (int64_t)k.m * k.m;
+        k.tm = k.m / tile;
+        k.tn = k.n / tile;
+        k.batch = (int)r.batch;
+        k.base = base;
+        base += k.batch;
+    }
+    for (int q = 0; q < p.nq; ++q) {
+        int g = 0, pp = 0, u = 0;
+        for (int b = 0; b < nbanks; ++b) {
+            const PersistBank& k = p.bank[b];
+            const int first = ((q - k.base) % p.nq + p.nq) % p.nq;
+            const int ls = first < k.batch ? (k.batch - first + p.nq - 1) / p.nq : 0;
+            p.ls[q][b] = ls;
+            g += ls * sym_count(k.tm);
+            pp += ls * sym_count(k.tm);
+            u += ls * k.tm * k.tn;
+        }
+        p.blk_g[q] = g;
+        p.blk_p[q] = pp;
+        p.per_round[q] = g + pp + u;
+    }
+    for (int t = 0; t < steps; ++t) {
+        p.coef[t][0] = coef[t].a;
+        p.coef[t][1] = coef[t].b;
+        p.coef[t][2] = coef[t].c;
     }
     if (tile == 256) {
         // one 8-wavefront workgroup per CU (its 128 KiB ring fills the LDS)
-        const dim3 grid((unsigned)d.cus);
-        if (tall) ns_persist_kernel<true, Cfg256><<<grid, Cfg256::NT, 0, stream>>>(p);
-        else ns_persist_kernel<false, Cfg256><<<grid, Cfg256::NT, 0, stream>>>(p);
+        ns_persist_kernel<Cfg256><<<dim3((unsigned)d.cus), Cfg256::NT, 0, stream>>>(p);
     } else {
         // two 4-wavefront workgroups per CU
-        const dim3 grid((unsigned)(2 * d.cus));
-        if (tall) ns_persist_kernel<true, Cfg128><<<grid, Cfg128::NT, 0, stream>>>(p);
-        else ns_persist_kernel<false, Cfg128><<<grid, Cfg128::NT, 0, stream>>>(p);
+        ns_persist_kernel<Cfg128><<<dim3((unsigned)(2 * d.cus)), Cfg128::NT, 0, stream>>>(p);
     }
     return hipGetLastError();
 }

@@ -167,13 +167,11 @@ __global__ void __launch_bounds__(256) sumsq_kernel(const uint16_t* __restrict__
 
 __global__ void __launch_bounds__(64) ns_scale_kernel(const float* __restrict__ partials, int nchunks, float eps,
                                                       float* __restrict__ scale, int* __restrict__ live,
-                                                      int* __restrict__ sync) {
+                                                      int* __restrict__ heads, int* __restrict__ ctr) {
     const int slot = blockIdx.x;
-    if (sync) {
-        // persistent kernel state: queue heads and error word [0, 32), slot counters [32, 32 + batch)
-        if (slot == 0 && threadIdx.x < 32) sync[threadIdx.x] = 0;
-        if (threadIdx.x == 0) sync[32 + slot] = 0;
-    }
+    // persistent kernel state: queue heads and error word, and this slot's counter
+    if (heads && slot == 0 && threadIdx.x < 32) heads[threadIdx.x] = 0;
+    if (ctr && threadIdx.x == 0) ctr[slot] = 0;
     float acc = 0.f;
     for (int i = threadIdx.x; i < nchunks; i += 64) acc += partials[(int64_t)slot * nchunks + i];
     acc = wave_sum(acc);
@@ -271,8 +269,8 @@ hipError_t launch_sumsq(const uint16_t* x, float* partials, int64_t batch, int64
 }
 
 hipError_t launch_ns_scale(const float* partials, int nchunks, int64_t batch, float eps, float* scale, int* live,
-                           int* sync, hipStream_t stream) {
-    ns_scale_kernel<<<(unsigned)batch, 64, 0, stream>>>(partials, nchunks, eps, scale, live, sync);
+                           int* heads, int* ctr, hipStream_t stream) {
+    ns_scale_kernel<<<(unsigned)batch, 64, 0, stream>>>(partials, nchunks, eps, scale, live, heads, ctr);
     return hipGetLastError();
 }
 

@@ -62,7 +62,10 @@ def test_workspace_queries(L):
     assert L.mb_ns_workspace_bytes(1, -1, 768) == 0
     b = api.mb_bank(40, 768, 768, api.MB_BF16, 1.0, 1.0, 0x10000, 0x20000, 0x30000, 0x40000, None, None, None)
     arr = (api.mb_bank * 2)(b, b)
-    assert L.mb_step_workspace_bytes(arr, 2) == 2 * L.mb_step_workspace_bytes(arr, 1) == 2 * w1
+    # per bank the Newton-Schulz workspace, plus one small block of queue heads and slot counters for
+    # the persistent launch over all banks
+    assert 2 * w1 < L.mb_step_workspace_bytes(arr, 2) <= 2 * w1 + 4096
+    assert w1 < L.mb_step_workspace_bytes(arr, 1) <= w1 + 4096
     assert L.mb_step_workspace_bytes(arr, 0) == 0
 
 
