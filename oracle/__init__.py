@@ -20,6 +20,8 @@ of the pages it follows.  The pages are cited by title and section:
 * "GPT-2 Medium 25.29-minute record" -- the walkthrough of track-2 Record 7;
   section 4.1 gives the bf16 + uint16 mantissa apply, section 4.2 the five
   quintic iterations.
+* "Unified zero-copy optimizer and transposed LM head", section 2.2, also
+  gives the two tied-embedding transposes (``oracle/transpose.py``).
 * "U-Net skips and doubled LR" -- the walkthrough of the 2024-11-10 record;
   its "four optimizers" section gives backend_steps=5, nesterov and the
   max(1, rows/cols)**0.5 scale.
@@ -50,3 +52,4 @@ from .muon import (  # noqa: F401
     step_scalars,
     split,
 )
+from .transpose import transpose_add, transpose_copy  # noqa: F401
