@@ -155,6 +155,19 @@ mb_status mp_apply_update(uint16_t *w_hi, uint16_t *w_lo, const uint16_t *v,
                           int64_t batch, int64_t slot_numel, float eff_lr, float decay,
                           const float *lr_mul_per_slot, void *stream);
 
+/* The tied-embedding transposes of the "Unified zero-copy optimizer and
+ * transposed LM head" page, section 2.2 (LM head stored as (768, 50304), the
+ * embedding as (50304, 768)): for src [rows, cols] and dst [cols, rows], both
+ * dense row-major device buffers that must not overlap,
+ *   transpose_copy:  dst[j][i] = src[i][j], elem_bytes 2 or 4 (the bits are copied);
+ *   transpose_add:   dst[j][i] = RN(dst[j][i] + src[i][j]), dtype MB_F32 or MB_BF16,
+ *                    one round-to-nearest-even of the exact sum.
+ * Pointers must be aligned to the element size (16-byte aligned buffers whose
+ * rows are whole 16-byte chunks take the tiled fast path).  Enqueued on
+ * `stream`; no workspace. */
+mb_status transpose_copy(void *dst, const void *src, int64_t rows, int64_t cols, int32_t elem_bytes, void *stream);
+mb_status transpose_add(void *dst, const void *src, int64_t rows, int64_t cols, int32_t dtype, void *stream);
+
 /* How stage 2 is scheduled (process-wide; the arithmetic is the same either way).
  *   0 (default): when both sides of a slot are multiples of 256, every round of a
  *     bank runs in one persistent launch: the 256x256 output tiles of all three

@@ -59,7 +59,7 @@ _lib = None
 
 EXPORTED = ("mb_default_hparams", "mb_status_string", "mb_last_error", "mb_version", "mb_step_workspace_bytes",
             "mb_ns_workspace_bytes", "muon_bank_step", "muon_momentum_update", "ns_orthogonalize_batched",
-            "ns_orthogonalize_batched_sched", "mp_apply_update", "mb_ns_set_path", "mb_timing_enable", "mb_timing_read")
+            "ns_orthogonalize_batched_sched", "mp_apply_update", "transpose_copy", "transpose_add", "mb_ns_set_path", "mb_timing_enable", "mb_timing_read")
 
 
 def lib() -> ctypes.CDLL:
@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
         "ns_orthogonalize_batched_sched": (i32, [vp, vp, i64, i64, i64, i32, vp, f64, vp, sz, vp]),
         "mp_apply_update": (i32, [vp, vp, vp, i64, i64, f32, f32, vp, vp]),
         "mb_ns_set_path": (i32, [i32]),
+        "transpose_copy": (i32, [vp, vp, i64, i64, i32, vp]),
+        "transpose_add": (i32, [vp, vp, i64, i64, i32, vp]),
         "mb_timing_enable": (None, [i32]),
         "mb_timing_read": (i32, [ctypes.POINTER(mb_kernel_time), i32]),
     }
@@ -283,6 +285,27 @@ def mp_apply_update(w_hi: torch.Tensor, w_lo: torch.Tensor, v: torch.Tensor, eff
         _dense(lr_mul_per_slot, "lr_mul_per_slot", 4)
     _check(lib().mp_apply_update(_ptr(w_hi), _ptr(w_lo), _ptr(v), batch, slot, float(eff_lr), float(decay),
                                  _ptr(lr_mul_per_slot), _stream(stream)))
+
+
+def transpose_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
+    """dst [cols, rows] = src [rows, cols] transposed (bits copied; 2- or 4-byte elements)."""
+    if src.dim() != 2 or dst.shape != (src.shape[1], src.shape[0]) or dst.element_size() != src.element_size():
+        raise ValueError("dst must be src's transpose shape with the same element size")
+    _dense(src, "src", (2, 4))
+    _dense(dst, "dst", src.element_size())
+    _check(lib().transpose_copy(_ptr(dst), _ptr(src), src.shape[0], src.shape[1], src.element_size(), _stream(stream)))
+
+
+def transpose_add(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
+    """dst [cols, rows] += src [rows, cols] transposed, one rounding (float32 or bfloat16)."""
+    if src.dim() != 2 or dst.shape != (src.shape[1], src.shape[0]) or dst.dtype != src.dtype:
+        raise ValueError("dst must be src's transpose shape with the same dtype")
+    if src.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("transpose_add takes float32 or bfloat16")
+    _dense(src, "src", (2, 4))
+    _dense(dst, "dst", src.element_size())
+    dt = MB_F32 if src.dtype == torch.float32 else MB_BF16
+    _check(lib().transpose_add(_ptr(dst), _ptr(src), src.shape[0], src.shape[1], dt, _stream(stream)))
 
 
 def mb_ns_set_path(path: int) -> int:

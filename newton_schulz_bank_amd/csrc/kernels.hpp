@@ -88,4 +88,8 @@ struct NsSmall {
 bool ns_small_eligible(int64_t rows, int64_t cols, int steps);
 hipError_t ns_small(const NsSmall& r, hipStream_t stream);
 
+// dst [cols, rows] = src^T (add: dst += src^T, one rounding), elements of 2 or 4 bytes.
+hipError_t launch_transpose(void* dst, const void* src, int64_t rows, int64_t cols, int elem_bytes, bool add,
+                            hipStream_t stream);
+
 }  // namespace mb

@@ -610,6 +610,43 @@ mb_status muon_bank_step(const mb_bank* banks, int32_t num_banks, const mb_hpara
     return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+mb_status transpose_impl(void* dst, const void* src, int64_t rows, int64_t cols, int es, bool add, const char* what,
+                         void* stream) {
+    if (!dst || !src) return fail(MB_ERR_NULL, "%s: null pointer", what);
+    mb_status s = check_shape(1, rows, cols, what);
+    if (s != MB_OK) return s;
+    if (((uintptr_t)dst | (uintptr_t)src) % (uintptr_t)es != 0)
+        return fail(MB_ERR_ALIGN, "%s: pointers must be aligned to the %d-byte element", what, es);
+    const int64_t bytes = rows * cols * es;
+    s = check_no_overlap({{(uintptr_t)dst, (uintptr_t)dst + bytes, "dst"}, {(uintptr_t)src, (uintptr_t)src + bytes, "src"}});
+    if (s != MB_OK) return s;
+    Timer timer;
+    timer.begin(add ? "transpose_add" : "transpose_copy", (hipStream_t)stream);
+    hipError_t e = mb::launch_transpose(dst, src, rows, cols, es, add, (hipStream_t)stream);
+    timer.end((hipStream_t)stream);
+    if (e != hipSuccess) return fail(MB_ERR_HIP, "%s launch: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+mb_status transpose_copy(void* dst, const void* src, int64_t rows, int64_t cols, int32_t elem_bytes, void* stream) {
+    if (elem_bytes != 2 && elem_bytes != 4)
+        return fail(MB_ERR_DTYPE, "transpose_copy: elem_bytes must be 2 or 4 (got %d)", elem_bytes);
+    return transpose_impl(dst, src, rows, cols, elem_bytes, false, "transpose_copy", stream);
+}
+
+mb_status transpose_add(void* dst, const void* src, int64_t rows, int64_t cols, int32_t dtype, void* stream) {
+    if (dtype != MB_F32 && dtype != MB_BF16) return fail(MB_ERR_DTYPE, "transpose_add: dtype %d", dtype);
+    return transpose_impl(dst, src, rows, cols, dtype == MB_F32 ? 4 : 2, true, "transpose_add", stream);
+}
+
 int32_t mb_ns_set_path(int32_t path) {
     if (path != 0 && path != 1) return -1;
     return g_ns_path.exchange(path);

@@ -147,6 +147,14 @@ def test_stage_entry_point_validation_errors(L):
     assert L.ns_orthogonalize_batched_sched(p, p + (1 << 30), 2, 64, 64, 0, sched, 1e-7, ws, need, None) == VALUE
     assert L.ns_orthogonalize_batched_sched(p, p + (1 << 30), 2, 64, 64, 65, sched, 1e-7, ws, need, None) == VALUE
     assert L.ns_orthogonalize_batched_sched(p, p + (1 << 30), 2, 64, 64, 2, sched, 1e-7, ws, need - 1, None) == WORKSPACE
+    # transposes
+    assert L.transpose_copy(None, p, 8, 8, 2, None) == NULL
+    assert L.transpose_copy(p, p + (1 << 30), 8, 0, 2, None) == SHAPE
+    assert L.transpose_copy(p, p + (1 << 30), 8, 8, 3, None) == DTYPE
+    assert L.transpose_copy(p + 1, p + (1 << 30), 8, 8, 2, None) == ALIGN
+    assert L.transpose_copy(p, p + 64, 8, 8, 2, None) == ALIAS
+    assert L.transpose_add(p, p + (1 << 30), 8, 8, 5, None) == DTYPE
+    assert L.transpose_add(p + 2, p + (1 << 30), 8, 8, 0, None) == ALIGN
     # apply
     assert L.mp_apply_update(None, p, p, 1, 64, 0.02, 0.9998, None, None) == NULL
     assert L.mp_apply_update(p, p + (1 << 30), p + (2 << 30), 1, 0, 0.02, 0.9998, None, None) == SHAPE
