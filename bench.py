@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--config", type=int, default=1, help="workload id 0..4 (1 = attention bank, the metric's case)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-parity", action="store_true")
+    p.add_argument("--workload", default="bank", choices=("bank", "transpose"),
+                   help="bank: the Muon bank step (the headline); transpose: the tied-embedding transposes of "
+                        "one optimizer step at the LM-head size")
     p.add_argument("--ns-path", type=int, default=0, choices=(0, 1),
                    help="0: persistent Newton-Schulz kernel where the shape allows it; 1: one launch per contraction")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -82,6 +85,9 @@ def main():
     from newton_schulz_bank_amd.workloads import CONFIG_NAMES, CONFIGS, make_bank
 
     api.lib()    # fails loudly if libmuonbank.so is missing
+    if args.workload == "transpose":
+        bench_transpose(args, torch, api)
+        return
     api.mb_ns_set_path(args.ns_path)
     specs = CONFIGS[args.config]
     hosts = [make_bank(args.config, i) for i in range(len(specs))]
@@ -246,13 +252,27 @@ def cpu_baseline(specs, hosts, config):
         threads = os.cpu_count() or 1
     budget_s = 12.0
     flops, elapsed, desc = 0, 0.0, []
+    passes = 0
+    while elapsed < budget_s and passes < 16:
+        passes += 1
+        f_, e_, d_ = _oracle_pass(oracle, specs, hosts, budget_s - elapsed)
+        flops += f_
+        elapsed += e_
+        desc = d_
+    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"full oracle step (momentum, fp64 NS5, exact apply) on {'; '.join(desc)}, {passes} pass(es)",
+            "seconds": round(elapsed, 2), "host": platform.processor() or platform.machine()}
+
+
+def _oracle_pass(oracle, specs, hosts, budget_s):
+    flops, elapsed, desc = 0, 0.0, []
     for spec, h in zip(specs, hosts):
         live = list(spec.live_slots)
         take = []
         for s in live:
-            take.append(s)
             if elapsed >= budget_s:
                 break
+            take.append(s)
             sl = np.ascontiguousarray
             bf = spec.grad_dtype == "bf16"
             vals = (lambda a: a.astype(np.float64)) if not bf else oracle.bf16_bits_to_f64
@@ -265,12 +285,98 @@ def cpu_baseline(specs, hosts, config):
         desc.append(f"{len(take)} of {len(live)} live slots of {spec.name} ({spec.rows}x{spec.cols})")
         if elapsed >= budget_s:
             break
-    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": "full oracle step (momentum, fp64 NS5, exact apply) on " + "; ".join(desc),
-            "seconds": round(elapsed, 2), "host": platform.processor() or platform.machine()}
+    return flops, elapsed, desc
 
 
-def read_traffic(kernel: str, config: int):
+def bench_transpose(args, torch, api):
+    """The tied-embedding transposes of one optimizer step: the LM head's gradient (768, 50304) added
+    transposed into the embedding's (50304, 768), and the embedding's weights copied transposed into
+    the LM head, bf16, seeded synthetic data."""
+    import oracle
+    rows, cols = 768, 50304
+    rng = np.random.default_rng(7000)
+
+    def bf(shape, sd):
+        return oracle.f64_to_bf16_bits(oracle.round_to_bf16(rng.normal(0, sd, shape)))
+    lm_grad, embed_grad = bf((rows, cols), 1e-3), bf((cols, rows), 1e-3)
+    embed_w = bf((cols, rows), 0.02)
+
+    def dev(a):
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    d_lm_grad, d_embed_grad, d_embed_w = dev(lm_grad), dev(embed_grad), dev(embed_w)
+    d_lm_w = torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    # parity gate on sampled embedding rows
+    api.transpose_add(d_embed_grad, d_lm_grad)
+    api.transpose_copy(d_lm_w, d_embed_w)
+    torch.cuda.synchronize()
+    pick = np.sort(rng.choice(cols, 64, replace=False))
+    got_add = d_embed_grad.view(torch.int16).cpu().numpy().view(np.uint16)[pick]
+    want_add = oracle.transpose_add(embed_grad[pick], np.ascontiguousarray(lm_grad[:, pick]), oracle.BF16)
+    got_copy = d_lm_w.view(torch.int16).cpu().numpy().view(np.uint16)
+    parity = {"transpose_add_bit_exact_sampled": bool(np.array_equal(got_add, want_add)),
+              "transpose_copy_bit_exact": bool(np.array_equal(got_copy, oracle.transpose_copy(embed_w)))}
+    d_embed_grad = dev(embed_grad)
+    for _ in range(args.warmup):
+        api.transpose_add(d_embed_grad, d_lm_grad)
+        api.transpose_copy(d_lm_w, d_embed_w)
+    torch.cuda.synchronize()
+
+    def timed(fns):
+        """K back-to-back calls of fns between two HIP events on the launch stream: ms per call of fns."""
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(args.steps):
+            for fn in fns:
+                fn()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / args.steps
+
+    def add():
+        api.transpose_add(d_embed_grad, d_lm_grad)
+
+    def copy():
+        api.transpose_copy(d_lm_w, d_embed_w)
+    # the step (both transposes), then each kernel alone: a per-launch event pair would add
+    # microseconds to kernels this short
+    ms_per_step = timed([add, copy])
+    n = rows * cols * 2
+    alg = {"transpose_add": 3 * n, "transpose_copy": 2 * n}       # bytes per launch
+    kernels = {}
+    for name, fn in (("transpose_add", add), ("transpose_copy", copy)):
+        us = timed([fn]) * 1e3
+        kernels[name] = {"avg_us": round(us, 3), "gbps": round(alg[name] / (us * 1e-6) / 1e9, 1)}
+    dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
+    achieved = kernels[dom]["gbps"]
+    # CPU baseline: the oracle on a bounded slab of the same matrices
+    t0, moved, slabs = time.perf_counter(), 0, 0
+    while time.perf_counter() - t0 < 10.0 and slabs < 400:
+        c0 = (slabs * 2048) % cols
+        sl = slice(c0, min(c0 + 2048, cols))
+        oracle.transpose_add(embed_grad[sl], np.ascontiguousarray(lm_grad[:, sl]), oracle.BF16)
+        oracle.transpose_copy(np.ascontiguousarray(embed_w[sl]))
+        moved += 5 * rows * (sl.stop - sl.start) * 2
+        slabs += 1
+    cpu_s = time.perf_counter() - t0
+    out = {
+        "metric": "tied-embedding transposes (transpose_add + transpose_copy) HBM GB/s, 1xMI355X",
+        "value": round(5 * n / (ms_per_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "LM head (768, 50304) <-> embedding (50304, 768), bf16", "rows": rows, "cols": cols},
+        "kernels": kernels,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": read_traffic(dom, "transpose")},
+        "parity": parity,
+        "cpu_baseline": {"value": round(moved / cpu_s / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                         "sample": f"{slabs} slabs of 2048 embedding rows (add + copy)", "seconds": round(cpu_s, 2)},
+    }
+    print(json.dumps(out), flush=True)
+
+
+def read_traffic(kernel: str, config):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
     taken on the current kernel source; else None."""
     path = os.path.join(HERE, "profiles", "traffic.json")
@@ -278,7 +384,7 @@ def read_traffic(kernel: str, config: int):
         return None
     try:
         data = json.load(open(path))
-        entry = data.get(f"{kernel}:config{config}")
+        entry = data.get(f"{kernel}:config{config}" if isinstance(config, int) else f"{kernel}:{config}")
         if not entry:
             return None
         import hashlib
