@@ -108,10 +108,11 @@ def main():
     ws = torch.empty(api.mb_step_workspace_bytes(banks), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
-    # ---- parity gate on a sample (the full checks live in the test suite)
-    parity = None
-    if not args.no_parity:
-        parity = parity_check(api, specs, hosts, args.config)
+    # ---- one sampled slot stepped on the GPU (compared with the oracle in the CPU-baseline leg;
+    # the full parity checks live in the test suite)
+    sample = None
+    if not args.no_parity and not args.no_cpu_baseline:
+        sample = gpu_sample_step(api, specs[0], hosts[0])
 
     # ---- timed region: K whole steps back to back, every kernel bracketed by HIP events on the
     # launch stream (pooled events: nothing is created inside the loop); ms_per_step and the
@@ -196,20 +197,15 @@ def main():
                     for k, v in kernels.items()},
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
-        "parity": parity,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(specs, hosts, args.config)
+        out["cpu_baseline"], out["parity"] = cpu_baseline(specs, hosts, sample)
     print(json.dumps(out), flush=True)
 
 
-def parity_check(api, specs, hosts, config):
-    """One step on fresh copies of the inputs; sampled slots against the oracle."""
+def gpu_sample_step(api, spec, h):
+    """One step of the bank's first live slot on fresh copies of its inputs; the raw output bits."""
     import torch
-    sys.path.insert(0, HERE)
-    import oracle
-    bi = 0
-    spec, h = specs[bi], hosts[bi]
     slot = spec.live_slots[0]
     bf = spec.grad_dtype == "bf16"
     sl = lambda a: np.ascontiguousarray(a[slot:slot + 1])
@@ -222,17 +218,25 @@ def parity_check(api, specs, hosts, config):
     b.v_out = torch.empty(b.w_hi.shape, dtype=torch.int16, device="cuda")
     api.muon_bank_step([b])
     torch.cuda.synchronize()
+    mom = (b.momentum.view(torch.int16).cpu().numpy().view(np.uint16) if bf else b.momentum.cpu().numpy())
+    return {"bank": spec.name, "slot": slot, "v": b.v_out.cpu().numpy().view(np.uint16),
+            "w_hi": b.w_hi.cpu().numpy().view(np.uint16), "w_lo": b.w_lo.cpu().numpy().view(np.uint16),
+            "momentum": mom}
+
+
+def _sample_parity(oracle, spec, h, sample):
+    """The GPU's sampled slot against the oracle's step on the same inputs."""
+    slot = sample["slot"]
+    bf = spec.grad_dtype == "bf16"
+    sl = lambda a: np.ascontiguousarray(a[slot:slot + 1])
     vals = (lambda a: a.astype(np.float64)) if not bf else oracle.bf16_bits_to_f64
     ref = oracle.muon_bank_step(vals(sl(h["grad"])), vals(sl(h["momentum"])), sl(h["w_hi"]), sl(h["w_lo"]),
                                 oracle.F32 if not bf else oracle.BF16)
-    v = oracle.bf16_bits_to_f64(b.v_out.cpu().numpy().view(np.uint16))
+    v = oracle.bf16_bits_to_f64(sample["v"])
     err = float(np.linalg.norm(v - ref["v64"]) / max(np.linalg.norm(ref["v64"]), 1e-30))
-    w_hi_bits = b.w_hi.cpu().numpy().view(np.uint16)
-    w_lo_bits = b.w_lo.cpu().numpy().view(np.uint16)
     want = oracle.mp_apply_update(sl(h["w_hi"]), sl(h["w_lo"]), v, ref["scalars"].eta, ref["scalars"].decay)
-    ok_apply = bool(np.array_equal(w_hi_bits, want[0]) and np.array_equal(w_lo_bits, want[1]))
-    mom = b.momentum.float().cpu().numpy().astype(np.float64) if not bf else oracle.bf16_bits_to_f64(
-        b.momentum.view(torch.int16).cpu().numpy().view(np.uint16))
+    ok_apply = bool(np.array_equal(sample["w_hi"], want[0]) and np.array_equal(sample["w_lo"], want[1]))
+    mom = vals(sample["momentum"]) if bf else sample["momentum"].astype(np.float64)
     ok_mom = bool(np.array_equal(mom, ref["momentum"]))
     if not (ok_apply and ok_mom and err <= 3e-2):
         raise SystemExit(f"parity failure on {spec.name} slot {slot}: ns rel err {err}, apply {ok_apply}, "
@@ -241,31 +245,38 @@ def parity_check(api, specs, hosts, config):
             "momentum_bit_exact": ok_mom}
 
 
-def cpu_baseline(specs, hosts, config):
-    """The oracle as it stands, on a bounded sample of the same workload, on the host's cores."""
+def cpu_baseline(specs, hosts, sample=None):
+    """The oracle as it stands, on a bounded sample of the same workload, on the host's cores.  With a
+    GPU sample (gpu_sample_step), the oracle's step of that slot is also compared with it; returns
+    (baseline, parity or None)."""
     sys.path.insert(0, HERE)
     import oracle
+    parity = _sample_parity(oracle, specs[0], hosts[0], sample) if sample is not None else None
     try:
         from threadpoolctl import threadpool_info
         threads = max([t.get("num_threads", 1) for t in threadpool_info() if t.get("user_api") == "blas"] or [1])
     except Exception:
         threads = os.cpu_count() or 1
     budget_s = 12.0
-    flops, elapsed, desc = 0, 0.0, []
+    flops, elapsed, counts = 0, 0.0, {}
     passes = 0
     while elapsed < budget_s and passes < 16:
         passes += 1
-        f_, e_, d_ = _oracle_pass(oracle, specs, hosts, budget_s - elapsed)
+        f_, e_, c_ = _oracle_pass(oracle, specs, hosts, budget_s - elapsed)
         flops += f_
         elapsed += e_
-        desc = d_
+        for k, v in c_.items():
+            counts[k] = counts.get(k, 0) + v
+    desc = [f"{counts[spec.name]} slot-steps over the {len(spec.live_slots)} live slots of {spec.name} "
+            f"({spec.rows}x{spec.cols})" for spec in specs if spec.name in counts]
     return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"full oracle step (momentum, fp64 NS5, exact apply) on {'; '.join(desc)}, {passes} pass(es)",
-            "seconds": round(elapsed, 2), "host": platform.processor() or platform.machine()}
+            "sample": f"full oracle step (momentum, fp64 NS5, exact apply), one slot at a time: {'; '.join(desc)}",
+            "seconds": round(elapsed, 2), "host": platform.processor() or platform.machine()}, parity
 
 
 def _oracle_pass(oracle, specs, hosts, budget_s):
-    flops, elapsed, desc = 0, 0.0, []
+    """One pass over the live slots of every bank, until the budget runs out: (flops, seconds, slots per bank)."""
+    flops, elapsed, counts = 0, 0.0, {}
     for spec, h in zip(specs, hosts):
         live = list(spec.live_slots)
         take = []
@@ -282,40 +293,33 @@ def _oracle_pass(oracle, specs, hosts, budget_s):
             elapsed += time.perf_counter() - t0
             f = ns_flops_per_slot(spec.rows, spec.cols)
             flops += sum(f.values())
-        desc.append(f"{len(take)} of {len(live)} live slots of {spec.name} ({spec.rows}x{spec.cols})")
+        counts[spec.name] = len(take)
         if elapsed >= budget_s:
             break
-    return flops, elapsed, desc
+    return flops, elapsed, counts
 
 
 def bench_transpose(args, torch, api):
     """The tied-embedding transposes of one optimizer step: the LM head's gradient (768, 50304) added
     transposed into the embedding's (50304, 768), and the embedding's weights copied transposed into
     the LM head, bf16, seeded synthetic data."""
-    import oracle
+    from newton_schulz_bank_amd.workloads import random_bf16_matrices
     rows, cols = 768, 50304
-    rng = np.random.default_rng(7000)
-
-    def bf(shape, sd):
-        return oracle.f64_to_bf16_bits(oracle.round_to_bf16(rng.normal(0, sd, shape)))
-    lm_grad, embed_grad = bf((rows, cols), 1e-3), bf((cols, rows), 1e-3)
-    embed_w = bf((cols, rows), 0.02)
+    lm_grad = random_bf16_matrices(7001, 1, rows, cols, 1e-3)[0]
+    embed_grad = random_bf16_matrices(7002, 1, cols, rows, 1e-3)[0]
+    embed_w = random_bf16_matrices(7003, 1, cols, rows, 0.02)[0]
 
     def dev(a):
         return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
     d_lm_grad, d_embed_grad, d_embed_w = dev(lm_grad), dev(embed_grad), dev(embed_w)
     d_lm_w = torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
-    # parity gate on sampled embedding rows
+    # one call of each on the inputs, kept for the CPU-baseline leg's comparison with the oracle
     api.transpose_add(d_embed_grad, d_lm_grad)
     api.transpose_copy(d_lm_w, d_embed_w)
     torch.cuda.synchronize()
-    pick = np.sort(rng.choice(cols, 64, replace=False))
-    got_add = d_embed_grad.view(torch.int16).cpu().numpy().view(np.uint16)[pick]
-    want_add = oracle.transpose_add(embed_grad[pick], np.ascontiguousarray(lm_grad[:, pick]), oracle.BF16)
+    got_add = d_embed_grad.view(torch.int16).cpu().numpy().view(np.uint16)
     got_copy = d_lm_w.view(torch.int16).cpu().numpy().view(np.uint16)
-    parity = {"transpose_add_bit_exact_sampled": bool(np.array_equal(got_add, want_add)),
-              "transpose_copy_bit_exact": bool(np.array_equal(got_copy, oracle.transpose_copy(embed_w)))}
     d_embed_grad = dev(embed_grad)
     for _ in range(args.warmup):
         api.transpose_add(d_embed_grad, d_lm_grad)
@@ -349,16 +353,8 @@ def bench_transpose(args, torch, api):
         kernels[name] = {"avg_us": round(us, 3), "gbps": round(alg[name] / (us * 1e-6) / 1e9, 1)}
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
     achieved = kernels[dom]["gbps"]
-    # CPU baseline: the oracle on a bounded slab of the same matrices
-    t0, moved, slabs = time.perf_counter(), 0, 0
-    while time.perf_counter() - t0 < 10.0 and slabs < 400:
-        c0 = (slabs * 2048) % cols
-        sl = slice(c0, min(c0 + 2048, cols))
-        oracle.transpose_add(embed_grad[sl], np.ascontiguousarray(lm_grad[:, sl]), oracle.BF16)
-        oracle.transpose_copy(np.ascontiguousarray(embed_w[sl]))
-        moved += 5 * rows * (sl.stop - sl.start) * 2
-        slabs += 1
-    cpu_s = time.perf_counter() - t0
+    cpu, parity = (None, None) if args.no_cpu_baseline else _transpose_cpu_baseline(
+        lm_grad, embed_grad, embed_w, got_add, got_copy)
     out = {
         "metric": "tied-embedding transposes (transpose_add + transpose_copy) HBM GB/s, 1xMI355X",
         "value": round(5 * n / (ms_per_step * 1e-3) / 1e9, 1),
@@ -369,11 +365,35 @@ def bench_transpose(args, torch, api):
         "kernels": kernels,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": read_traffic(dom, "transpose")},
-        "parity": parity,
-        "cpu_baseline": {"value": round(moved / cpu_s / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-                         "sample": f"{slabs} slabs of 2048 embedding rows (add + copy)", "seconds": round(cpu_s, 2)},
     }
+    if cpu is not None:
+        out["cpu_baseline"], out["parity"] = cpu, parity
     print(json.dumps(out), flush=True)
+
+
+def _transpose_cpu_baseline(lm_grad, embed_grad, embed_w, got_add, got_copy):
+    """The oracle's transposes on a bounded slab of the same matrices, timed on one host core; the
+    GPU's results are compared with the oracle's on 64 sampled embedding rows (add) and in full (copy)."""
+    sys.path.insert(0, HERE)
+    import oracle
+    rows, cols = lm_grad.shape
+    pick = np.sort(np.random.default_rng(7000).choice(cols, 64, replace=False))
+    want_add = oracle.transpose_add(embed_grad[pick], np.ascontiguousarray(lm_grad[:, pick]), oracle.BF16)
+    parity = {"transpose_add_bit_exact_sampled": bool(np.array_equal(got_add[pick], want_add)),
+              "transpose_copy_bit_exact": bool(np.array_equal(got_copy, oracle.transpose_copy(embed_w)))}
+    if not all(parity.values()):
+        raise SystemExit(f"transpose parity failure: {parity}")
+    t0, moved, slabs = time.perf_counter(), 0, 0
+    while time.perf_counter() - t0 < 10.0 and slabs < 400:
+        c0 = (slabs * 2048) % cols
+        sl = slice(c0, min(c0 + 2048, cols))
+        oracle.transpose_add(embed_grad[sl], np.ascontiguousarray(lm_grad[:, sl]), oracle.BF16)
+        oracle.transpose_copy(np.ascontiguousarray(embed_w[sl]))
+        moved += 5 * rows * (sl.stop - sl.start) * 2
+        slabs += 1
+    cpu_s = time.perf_counter() - t0
+    return ({"value": round(moved / cpu_s / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+             "sample": f"{slabs} slabs of 2048 embedding rows (add + copy)", "seconds": round(cpu_s, 2)}, parity)
 
 
 def read_traffic(kernel: str, config):
