@@ -50,13 +50,32 @@ __device__ __forceinline__ int ks(int R) { return (R & 7) ^ ((R >> 3) & 1); }
 // chunks x 2 halves), which the XOR with 4*(k & 3) spreads over all 64 banks.
 __device__ __forceinline__ int ms(int k) { return 4 * (k & 3); }
 
-// MUBUF load of 16 bytes per lane straight into LDS (lane l -> LDS base + 16*l).  Unlike the
-// FLAT-encoded global_load_lds it is tracked by vmcnt alone, so waiting for LDS reads never
-// waits for copies still in flight; reads past the descriptor's size return zeros.
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-extern "C" __device__ void mb_raw_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) uint32_t* lds,
-                                                  int size, int voffset, int soffset, int offset, int aux)
-    __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// MUBUF load of 16 bytes per lane straight into LDS (lane l -> LDS base + 16*l; M0 holds the LDS
+// base, saved and restored around the copy).  Unlike the FLAT-encoded global_load_lds it is
+// tracked by vmcnt alone, so waiting for LDS reads never waits for copies still in flight; reads
+// past the descriptor's size return zeros.  It is issued from inline assembly so that the compiler
+// does not see an LDS write: seeing one, it orders later LDS reads after it with vmcnt(0) whenever
+// its alias analysis cannot separate the two ring stages (it could not in some of the tile's
+// instantiations, which then waited for every next-stage copy right after issuing it).  Every wait
+// on these copies is the explicit one the caller places.
+template <int POL>
+__device__ __forceinline__ void lds_dma16(i32x4 rsrc, const uint16_t* lds, int voffset) {
+    const uint32_t a = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)lds);
+    int save;
+    if (POL == POL_SC1)
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+            "buffer_load_dwordx4 %2, %3, 0 offen sc1 lds\n\ts_mov_b32 m0, %0\n\ts_nop 0"
+            : "=&s"(save) : "s"(a), "v"(voffset), "s"(rsrc) : "memory");
+    else
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+            "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0\n\ts_nop 0"
+            : "=&s"(save) : "s"(a), "v"(voffset), "s"(rsrc) : "memory");
+}
 
 // Buffer descriptor of `bytes` bytes at `base` (raw buffer, stride 0; word 3 as for every gfx9 part).
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
@@ -89,8 +108,7 @@ __device__ __forceinline__ void load_tile_lds(i32x4 rsrc, int ld, int mn0, int k
             const int c = (lane % CPR) ^ ms(k);
             elem = (k0 + k) * ld + mn0 + c * 8;
         }
-        mb_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) uint32_t*)(lds + q * 512), 16, elem * 2, 0, 0,
-                               POL);
+        lds_dma16<POL>(rsrc, lds + q * 512, elem * 2);
     }
 }
 
@@ -252,8 +270,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, uint16_t* smem, int
             const int e = q * 64 + lane;
             const int i = e / CPRO, c = (e % CPRO) ^ (i % CW);
             const int elem = (i0 + i) * jb.ldx + j0 + c * 8;
-            mb_raw_buffer_load_lds(jb.X, (__attribute__((address_space(3))) uint32_t*)(st + q * 512), 16, elem * 2, 0,
-                                   0, POL);
+            lds_dma16<POL>(jb.X, st + q * 512, elem * 2);
         }
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
