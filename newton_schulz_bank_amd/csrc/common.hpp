@@ -17,6 +17,14 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 #define MB_LDS __attribute__((address_space(3)))
+// LDS pointer from a generic pointer into LDS: the low 32 bits of such a pointer are its LDS byte
+// address.  (An address-space cast would add a null check, which some instantiations of the tile
+// turned into an instruction the backend rejects.)
+template <class T>
+__device__ __forceinline__ MB_LDS T* lds_ptr(const void* p) {
+    return (MB_LDS T*)(uint32_t)(uintptr_t)p;
+}
+typedef MB_LDS uint16_t lds_u16;
 
 // bf16 bits -> float (exact).
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }

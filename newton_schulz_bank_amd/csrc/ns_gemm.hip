@@ -121,8 +121,8 @@ __device__ __forceinline__ bf16x8 read_frag(const uint16_t* lds, int mn_base, in
         const int krow = kk * 16 + 8 * (g >> 1) + s;
         const uint16_t* p0 = lds + krow * MP + col;
         const uint16_t* p1 = p0 + 4 * MP;
-        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MB_LDS i16x4*)(p0));
-        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MB_LDS i16x4*)(p1));
+        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(p0));
+        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(p1));
         i16x4 both[2] = {lo, hi};
         bf16x8 out;
         __builtin_memcpy(&out, both, 16);
@@ -349,7 +349,7 @@ __global__ void __launch_bounds__(C::NT, 2) ns_gemm_fast(GemmArgs args) {
         sig = (EPI == EPI_GRAM) ? s * s : s;
     }
     jb.sig = sig;
-    gemm_tile<P_KMAJOR, Q_KMAJOR, EPI, C, POL_DEFAULT>(jb, smem, (int)threadIdx.x);
+    gemm_tile<P_KMAJOR, Q_KMAJOR, EPI, C, POL_DEFAULT>(jb, (lds_u16*)smem, (int)threadIdx.x);
 }
 
 // Tile configuration of one contraction: 256x256 tiles move half the bytes per flop out of L2

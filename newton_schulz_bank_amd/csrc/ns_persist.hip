@@ -176,8 +176,8 @@ __global__ void __launch_bounds__(C::NT, 2) ns_persist_kernel(PersistArgs p) {
                     const float sc = bk.scale[slot];
                     jb.sig = sc * sc;
                 }
-                if (tall) gemm_tile<false, false, EPI_GRAM, C, POL_SC1>(jb, smem, ltid);
-                else gemm_tile<true, true, EPI_GRAM, C, POL_SC1>(jb, smem, ltid);
+                if (tall) gemm_tile<false, false, EPI_GRAM, C, POL_SC1>(jb, (lds_u16*)smem, ltid);
+                else gemm_tile<true, true, EPI_GRAM, C, POL_SC1>(jb, (lds_u16*)smem, ltid);
             }
         } else if (phase == 1) {
             if (live) {
@@ -194,7 +194,7 @@ __global__ void __launch_bounds__(C::NT, 2) ns_persist_kernel(PersistArgs p) {
                 jb.mirror = ti != tj;
                 jb.alpha = p.coef[t][2];
                 jb.beta = p.coef[t][1];
-                gemm_tile<true, true, EPI_POLY, C, POL_SC1>(jb, smem, ltid);
+                gemm_tile<true, true, EPI_POLY, C, POL_SC1>(jb, (lds_u16*)smem, ltid);
             }
         } else {
             // wide: X' (m x n) = a*X + B X;  tall: G' (n x m) = a*G + G B
@@ -218,8 +218,8 @@ __global__ void __launch_bounds__(C::NT, 2) ns_persist_kernel(PersistArgs p) {
                 jb.mirror = false;
                 jb.beta = p.coef[t][0];
                 if (t == 0) jb.sig = bk.scale[slot];
-                if (tall) gemm_tile<true, true, EPI_UPDATE, C, POL_SC1>(jb, smem, ltid);
-                else gemm_tile<true, false, EPI_UPDATE, C, POL_SC1>(jb, smem, ltid);
+                if (tall) gemm_tile<true, true, EPI_UPDATE, C, POL_SC1>(jb, (lds_u16*)smem, ltid);
+                else gemm_tile<true, false, EPI_UPDATE, C, POL_SC1>(jb, (lds_u16*)smem, ltid);
             } else if (last) {
                 // a zero slot's result is exactly zero
                 const int i0 = ti * kTile, j0 = tj * kTile;

@@ -61,9 +61,11 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 // instantiations, which then waited for every next-stage copy right after issuing it).  Every wait
 // on these copies is the explicit one the caller places.
 template <int POL>
-__device__ __forceinline__ void lds_dma16(i32x4 rsrc, const uint16_t* lds, int voffset) {
-    const uint32_t a = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)lds);
+__device__ __forceinline__ void lds_dma16(i32x4 rsrc, const lds_u16* lds, int voffset) {
+    const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+    // the descriptor is uniform; readfirstlane states it, so the "s" constraints always hold
+#pragma unroll
+    for (int w = 0; w < 4; ++w) rsrc[w] = __builtin_amdgcn_readfirstlane(rsrc[w]);
     int save;
     if (POL == POL_SC1)
         asm volatile(
@@ -91,7 +93,7 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
 // Copy one ROWS (mn) x 64 (k) operand tile into LDS: ROWS/8 instructions of 64 lanes x 16 B,
 // instruction q filling entries [64q, 64q + 64).
 template <bool KMAJOR, int ROWS, int NW, int POL>
-__device__ __forceinline__ void load_tile_lds(i32x4 rsrc, int ld, int mn0, int k0, uint16_t* lds, int wave,
+__device__ __forceinline__ void load_tile_lds(i32x4 rsrc, int ld, int mn0, int k0, lds_u16* lds, int wave,
                                               int lane) {
     constexpr int NI = ROWS / 8 / NW;
     constexpr int CPR = ROWS / 8;                         // chunks per k row (MN-major)
@@ -114,11 +116,11 @@ __device__ __forceinline__ void load_tile_lds(i32x4 rsrc, int ld, int mn0, int k
 
 // MFMA fragment (32 rows x 16 k; lane l holds row l%32, k = kk*16 + 8*(l/32) + 0..7) from a swizzled tile.
 template <bool KMAJOR, int ROWS>
-__device__ __forceinline__ bf16x8 read_frag_fast(const uint16_t* lds, int mn_base, int kk, int lane) {
+__device__ __forceinline__ bf16x8 read_frag_fast(const lds_u16* lds, int mn_base, int kk, int lane) {
     if (KMAJOR) {
         const int R = mn_base + (lane & 31);
         const int c = 2 * kk + (lane >> 5);
-        return *reinterpret_cast<const bf16x8*>(lds + (R * 8 + (c ^ ks(R))) * 8);
+        return *(const MB_LDS bf16x8*)(lds + (R * 8 + (c ^ ks(R))) * 8);
     } else {
         constexpr int CPR = ROWS / 8;
         // ds_read_b64_tr_b16: within each 16-lane group, source lane 4s+q names k row s, columns
@@ -127,11 +129,11 @@ __device__ __forceinline__ bf16x8 read_frag_fast(const uint16_t* lds, int mn_bas
         const int mn = mn_base + 16 * (g & 1) + 4 * q;
         const int k = kk * 16 + 8 * (g >> 1) + s;
         const int c = mn >> 3, half = (mn >> 2) & 1;
-        const uint16_t* p0 = lds + (k * CPR + (c ^ ms(k))) * 8 + half * 4;
+        const lds_u16* p0 = lds + (k * CPR + (c ^ ms(k))) * 8 + half * 4;
         const int k4 = k + 4;
-        const uint16_t* p1 = lds + (k4 * CPR + (c ^ ms(k4))) * 8 + half * 4;
-        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MB_LDS i16x4*)(p0));
-        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MB_LDS i16x4*)(p1));
+        const lds_u16* p1 = lds + (k4 * CPR + (c ^ ms(k4))) * 8 + half * 4;
+        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MB_LDS i16x4*)p0);
+        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MB_LDS i16x4*)p1);
         i16x4 both[2] = {lo, hi};
         bf16x8 out;
         __builtin_memcpy(&out, both, 16);
@@ -169,7 +171,7 @@ struct TileJob {
 // through an opaque copy made inside the loop, so the per-lane address arithmetic is recomputed
 // per tile instead of being hoisted out of the loop and held in registers across it.
 template <bool P_KMAJOR, bool Q_KMAJOR, int EPI, class C, int POL>
-__device__ __forceinline__ void gemm_tile(const TileJob& jb, uint16_t* smem, int tid) {
+__device__ __forceinline__ void gemm_tile(const TileJob& jb, lds_u16* smem, int tid) {
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave / C::WN, wn = wave % C::WN;
@@ -184,8 +186,14 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, uint16_t* smem, int
             for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
     const int KT = jb.K / kBK;
+    // a diagonal tile of a symmetric product (X X^T, A A) has P == Q: its operand is copied once
+    // and both fragment sets read it
+    const bool same = P_KMAJOR == Q_KMAJOR && C::BM == C::BN &&
+                      __builtin_amdgcn_readfirstlane((int)(i0 == j0 && jb.P[0] == jb.Q[0] && jb.P[1] == jb.Q[1] &&
+                                                           jb.ldp == jb.ldq)) != 0;
+    const int qoff = same ? 0 : C::BM * kBK;            // Q's offset in a ring stage (elements)
     load_tile_lds<P_KMAJOR, C::BM, C::NW, POL>(jb.P, jb.ldp, i0, 0, smem, wave, lane);
-    load_tile_lds<Q_KMAJOR, C::BN, C::NW, POL>(jb.Q, jb.ldq, j0, 0, smem + C::BM * kBK, wave, lane);
+    if (!same) load_tile_lds<Q_KMAJOR, C::BN, C::NW, POL>(jb.Q, jb.ldq, j0, 0, smem + C::BM * kBK, wave, lane);
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
 
@@ -197,16 +205,18 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, uint16_t* smem, int
     for (int a = 0; a < C::FM; ++a) pf[0][a] = read_frag_fast<P_KMAJOR, C::BM>(smem, wm * C::TM + a * 32, 0, lane);
 #pragma unroll
     for (int b = 0; b < C::FN; ++b)
-        qf[0][b] = read_frag_fast<Q_KMAJOR, C::BN>(smem + C::BM * kBK, wn * C::TN + b * 32, 0, lane);
+        qf[0][b] = read_frag_fast<Q_KMAJOR, C::BN>(smem + qoff, wn * C::TN + b * 32, 0, lane);
 
     for (int kt = 0; kt < KT; ++kt) {
         const int cur = kt & 1;
-        const uint16_t* lp = smem + cur * C::STAGE;
+        const lds_u16* lp = smem + cur * C::STAGE;
         const bool more = kt + 1 < KT;
         if (more) {
-            uint16_t* np = smem + (cur ^ 1) * C::STAGE;
+            lds_u16* np = smem + (cur ^ 1) * C::STAGE;
             load_tile_lds<P_KMAJOR, C::BM, C::NW, POL>(jb.P, jb.ldp, i0, (kt + 1) * kBK, np, wave, lane);
-            load_tile_lds<Q_KMAJOR, C::BN, C::NW, POL>(jb.Q, jb.ldq, j0, (kt + 1) * kBK, np + C::BM * kBK, wave, lane);
+            if (!same)
+                load_tile_lds<Q_KMAJOR, C::BN, C::NW, POL>(jb.Q, jb.ldq, j0, (kt + 1) * kBK, np + C::BM * kBK, wave,
+                                                           lane);
         }
 #pragma unroll
         for (int kk = 0; kk < kBK / 16; ++kk) {
@@ -217,18 +227,18 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, uint16_t* smem, int
                     pf[nb][a] = read_frag_fast<P_KMAJOR, C::BM>(lp, wm * C::TM + a * 32, kk + 1, lane);
 #pragma unroll
                 for (int b = 0; b < C::FN; ++b)
-                    qf[nb][b] = read_frag_fast<Q_KMAJOR, C::BN>(lp + C::BM * kBK, wn * C::TN + b * 32, kk + 1, lane);
+                    qf[nb][b] = read_frag_fast<Q_KMAJOR, C::BN>(lp + qoff, wn * C::TN + b * 32, kk + 1, lane);
             } else if (more) {
                 // every wave's reads of this stage are done and the next stage has landed
                 __builtin_amdgcn_s_waitcnt(0);
                 __builtin_amdgcn_s_barrier();
-                const uint16_t* np = smem + (cur ^ 1) * C::STAGE;
+                const lds_u16* np = smem + (cur ^ 1) * C::STAGE;
 #pragma unroll
                 for (int a = 0; a < C::FM; ++a)
                     pf[nb][a] = read_frag_fast<P_KMAJOR, C::BM>(np, wm * C::TM + a * 32, 0, lane);
 #pragma unroll
                 for (int b = 0; b < C::FN; ++b)
-                    qf[nb][b] = read_frag_fast<Q_KMAJOR, C::BN>(np + C::BM * kBK, wn * C::TN + b * 32, 0, lane);
+                    qf[nb][b] = read_frag_fast<Q_KMAJOR, C::BN>(np + qoff, wn * C::TN + b * 32, 0, lane);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -256,7 +266,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, uint16_t* smem, int
     constexpr int CH = C::BM * CPRO;                    // 16-byte chunks per tile
     static_assert(C::BM == C::BN || EPI == EPI_UPDATE, "symmetric tiles are square");
     static_assert(CH % (64 * C::NW) == 0, "the aux copy splits evenly over the wavefronts");
-    uint16_t* st = smem;                                 // BM x BN bf16 staging tile (fits the ring)
+    lds_u16* st = smem;                                  // BM x BN bf16 staging tile (fits the ring)
     auto spos = [&](int i, int c) { return i * C::BN + ((c ^ (i % CW)) << 3); };
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
@@ -283,10 +293,10 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, uint16_t* smem, int
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int j = wn * C::TN + b * 32 + 8 * g + 4 * (lane >> 5);
-                uint16_t* p = st + spos(i, j >> 3) + (j & 4);
+                lds_u16* p = st + spos(i, j >> 3) + (j & 4);
                 float av[4] = {0.f, 0.f, 0.f, 0.f};
                 if (EPI != EPI_GRAM) {
-                    const u32x2 wv = *reinterpret_cast<const u32x2*>(p);
+                    const u32x2 wv = *(const MB_LDS u32x2*)p;
                     av[0] = __uint_as_float(wv[0] << 16);
                     av[1] = __uint_as_float(wv[0] & 0xFFFF0000u);
                     av[2] = __uint_as_float(wv[1] << 16);
@@ -303,7 +313,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, uint16_t* smem, int
                 u32x2 wv;
                 wv[0] = f32x2_to_bf16x2_rne(y[0], y[1]);
                 wv[1] = f32x2_to_bf16x2_rne(y[2], y[3]);
-                *reinterpret_cast<u32x2*>(p) = wv;
+                *(MB_LDS u32x2*)p = wv;
             }
         }
     }
@@ -313,7 +323,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, uint16_t* smem, int
     for (int v = tid; v < CH; v += C::NT) {
         const int i = v / CPRO, c = v % CPRO;
         *reinterpret_cast<u32x4*>(jb.out + (int64_t)(i0 + i) * jb.ldo + j0 + c * 8) =
-            *reinterpret_cast<const u32x4*>(st + spos(i, c));
+            *(const MB_LDS u32x4*)(st + spos(i, c));
     }
     if (EPI != EPI_UPDATE && jb.mirror) {
         // unit (ib, jb16): tile rows [32 ib, 32 ib + 32) x columns [16 jb16, 16 jb16 + 16); the four
@@ -328,10 +338,10 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, uint16_t* smem, int
             const int ib = u % (C::BM / 32), jb16 = u / (C::BM / 32);
             const int i = ib * 32 + grp * 8;
             const int jc = jb16 * 16 + 4 * q4;
-            const uint16_t* pa = st + spos(i + s4, jc >> 3) + (jc & 7);
-            const uint16_t* pb = st + spos(i + 4 + s4, jc >> 3) + (jc & 7);
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MB_LDS i16x4*)(pa));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MB_LDS i16x4*)(pb));
+            const lds_u16* pa = st + spos(i + s4, jc >> 3) + (jc & 7);
+            const lds_u16* pb = st + spos(i + 4 + s4, jc >> 3) + (jc & 7);
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MB_LDS i16x4*)pa);
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MB_LDS i16x4*)pb);
             u32x4 w;
             w[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
             w[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);

@@ -63,8 +63,8 @@ __global__ void __launch_bounds__(kThreads) transpose16_kernel(uint16_t* __restr
         // lane 4s + q addresses tile row 8*ig + s (then + 4), columns 16*jg + 4q .. +3; lane t receives
         // column 16*jg + t of those rows: 8 consecutive src rows of one src column
         const uint16_t* pa = tile + (8 * ig + s4) * kP16 + 16 * jg + 4 * q4;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MB_LDS i16x4*)(pa));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MB_LDS i16x4*)(pa + 4 * kP16));
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(pa));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(pa + 4 * kP16));
         u32x4 w;
         w[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
         w[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
