@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--config", type=int, default=1, help="workload id 0..4 (1 = attention bank, the metric's case)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-parity", action="store_true")
+    p.add_argument("--time-every", type=int, default=10,
+                   help="bracket the kernels of every N-th timed step with HIP events (1 = every step)")
     p.add_argument("--workload", default="bank", choices=("bank", "transpose"),
                    help="bank: the Muon bank step (the headline); transpose: the tied-embedding transposes of "
                         "one optimizer step at the LM-head size")
@@ -116,23 +118,33 @@ def main():
 
     # ---- timed region: K whole steps back to back, every kernel bracketed by HIP events on the
     # launch stream (pooled events: nothing is created inside the loop); ms_per_step and the
-    # per-kernel durations come from this same region
+    # per-kernel durations come from this same region.  The kernels of every --time-every'th step
+    # are bracketed (each event pair costs the stream a few microseconds, so bracketing every
+    # launch would inflate the step time it is part of); their averages are over those launches.
     api.mb_timing_enable(True)
     for _ in range(args.warmup):
         api.muon_bank_step(banks, workspace=ws, stream=stream)
     torch.cuda.synchronize()
     api.mb_timing_read()
+    api.mb_timing_enable(False)
+    every = max(1, args.time_every)
+    sampled = 0
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record(stream)
-    for _ in range(args.steps):
+    for k in range(args.steps):
+        timed_step = k % every == 0
+        if timed_step:
+            api.mb_timing_enable(True)
+            sampled += 1
         api.muon_bank_step(banks, workspace=ws, stream=stream)
+        if timed_step:
+            api.mb_timing_enable(False)
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = start.elapsed_time(stop) / args.steps
     per_kernel = api.mb_timing_read()
-    api.mb_timing_enable(False)
 
     live_slots = sum(len(s.live_slots) for s in specs)
     # algorithmic flops by the kernel that does them: banks whose sides are multiples of 256 run
@@ -152,7 +164,7 @@ def main():
     kernels = {}
     for name, (n, tot) in per_kernel.items():
         per_launch = tot / n
-        kernels[name] = {"launches_per_step": n / args.steps, "avg_us": per_launch * 1e3, "ms_per_step": tot / args.steps}
+        kernels[name] = {"launches_per_step": n / sampled, "avg_us": per_launch * 1e3, "ms_per_step": tot / sampled}
     ns_ms = sum(kernels.get(k, {"ms_per_step": 0})["ms_per_step"] for k in alg)
     for k in alg:
         if k in kernels:
@@ -196,6 +208,7 @@ def main():
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
         "wall_s_timed": round(wall, 4),
+        "kernel_timing": {"steps_bracketed": sampled, "every": every},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

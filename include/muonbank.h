@@ -184,8 +184,10 @@ int32_t mb_ns_set_path(int32_t path);
  * launches is bracketed by two hipEvents on its stream; mb_timing_read waits
  * for them and returns, per kernel name, the launch count and the summed
  * duration in milliseconds.  Enabling creates a pool of events that reads hand
- * back, so a timed loop records events without creating them.  Timing never
- * changes a result. */
+ * back, so a timed loop records events without creating them; switching timing
+ * on and off between calls (to bracket only some of them) creates none either
+ * until half the pool is in use.  Each event pair costs the stream a few
+ * microseconds.  Timing never changes a result. */
 typedef struct {
     char name[48];
     int64_t launches;

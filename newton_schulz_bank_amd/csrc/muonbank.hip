@@ -655,6 +655,8 @@ int32_t mb_ns_set_path(int32_t path) {
 void mb_timing_enable(int32_t on) {
     std::lock_guard<std::mutex> lk(g_timing_mu);
     g_timing_on = on != 0;
+    // refill only when the pool runs low, so that switching timing on between steps creates no events
+    if (g_timing_on && g_event_pool.size() >= kEventPoolInit / 2) return;
     while (g_timing_on && g_event_pool.size() < kEventPoolInit) {
         hipEvent_t e;
         if (hipEventCreate(&e) != hipSuccess) break;
