@@ -88,6 +88,30 @@ __device__ __forceinline__ uint16_t odd53_to_bf16(double s) {
     return f32_to_bf16_rne(f);
 }
 
+// RN_bf16 of the exact sum a + b of two binary64 values (correct rounding, ties to even), the
+// same value as odd53_to_bf16(sum_round_odd(a, b)) at a fraction of the cost.  With s = RN53(a + b)
+// and f = RN32(s): a bf16 rounding boundary strictly between the exact sum and s, or between s
+// and f, would be a representable value closer than the one rounded to, so RN_bf16(f) is the
+// answer unless f is a bf16 midpoint.  Then the side of f the exact sum lies on decides: the
+// side of s if s != f (it is the same side), else the sign of the TwoSum error (zero: an
+// exact tie, to even).  Only lanes at a midpoint reach the slower part.
+__device__ __forceinline__ uint16_t sum_to_bf16(double a, double b) {
+    const double s = a + b;
+    const float f = (float)s;
+    const uint32_t fb = __float_as_uint(f);
+    if ((fb & 0xFFFFu) != 0x8000u) return f32_to_bf16_rne(f);
+    bool up;
+    const double fd = (double)f;
+    if (fd != s) {
+        up = fabs(s) > fabs(fd);
+    } else {
+        const double e = two_sum_err(a, b, s);
+        if (e == 0.0) return f32_to_bf16_rne(f);
+        up = (e > 0.0) == (s > 0.0);
+    }
+    return (uint16_t)((fb >> 16) + (up ? 1u : 0u));
+}
+
 // Wavefront (64-lane) sum with a fixed reduction tree.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -20,25 +20,24 @@ namespace mb {
 // momentum + Nesterov
 // ---------------------------------------------------------------------------
 
-// Exact products in binary64 (<=24-bit x <=24-bit significands), a
-// round-to-odd sum, then one rounding to the storage format: buf' and u are
-// the correctly rounded exact values.
+// Exact products in binary64 (<=24-bit x <=24-bit significands), then the
+// correctly rounded exact sum in the storage format: for float32 through a
+// round-to-odd binary64 sum, for bf16 with sum_to_bf16.  buf' and u are the
+// correctly rounded exact values.
 __device__ __forceinline__ void momentum_elem(float g, float b, float mu, float nu, float& buf_new_f32,
                                               uint16_t& buf_new_bf16, uint16_t& u_bits, bool f32_storage,
                                               float& u_val) {
     double p_buf = (double)mu * (double)b;
     double p_g = (double)nu * (double)g;
-    double s = sum_round_odd(p_buf, p_g);
     float stored;
     if (f32_storage) {
-        buf_new_f32 = odd53_to_f32(s);
+        buf_new_f32 = odd53_to_f32(sum_round_odd(p_buf, p_g));
         stored = buf_new_f32;
     } else {
-        buf_new_bf16 = odd53_to_bf16(s);
+        buf_new_bf16 = sum_to_bf16(p_buf, p_g);
         stored = bf16_to_f32(buf_new_bf16);
     }
-    double s2 = sum_round_odd(p_g, (double)mu * (double)stored);
-    u_bits = odd53_to_bf16(s2);
+    u_bits = sum_to_bf16(p_g, (double)mu * (double)stored);
     u_val = bf16_to_f32(u_bits);
 }
 
