@@ -99,17 +99,19 @@ __device__ __forceinline__ uint16_t sum_to_bf16(double a, double b) {
     const double s = a + b;
     const float f = (float)s;
     const uint32_t fb = __float_as_uint(f);
-    if ((fb & 0xFFFFu) != 0x8000u) return f32_to_bf16_rne(f);
-    bool up;
     const double fd = (double)f;
-    if (fd != s) {
-        up = fabs(s) > fabs(fd);
-    } else {
+    const bool mid = (fb & 0xFFFFu) == 0x8000u;
+    // selects, not branches, for the common cases: midpoints of f are frequent enough (a few in a
+    // hundred sums) that a branch on them would be taken by almost every wavefront
+    uint32_t h = f32_to_bf16_rne(f);
+    const uint32_t side = (fb >> 16) + (fabs(s) > fabs(fd) ? 1u : 0u);
+    h = (mid && fd != s) ? side : h;
+    if (mid && fd == s) {
+        // s itself is a midpoint (rare): the TwoSum error decides; zero is an exact tie
         const double e = two_sum_err(a, b, s);
-        if (e == 0.0) return f32_to_bf16_rne(f);
-        up = (e > 0.0) == (s > 0.0);
+        if (e != 0.0) h = (fb >> 16) + (((e > 0.0) == (s > 0.0)) ? 1u : 0u);
     }
-    return (uint16_t)((fb >> 16) + (up ? 1u : 0u));
+    return (uint16_t)h;
 }
 
 // Wavefront (64-lane) sum with a fixed reduction tree.
