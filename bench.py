@@ -35,6 +35,13 @@ def ns_flops_per_slot(rows: int, cols: int, steps: int = 5) -> dict:
     return {"ns_gram": steps * m * (m + 1) * n, "ns_poly": steps * m * m * (m + 1), "ns_update": steps * 2 * m * m * n}
 
 
+def ns_dense_flops_per_slot(rows: int, cols: int, steps: int = 5) -> int:
+    """Dense-equivalent flops of the same rounds, symmetric products counted in full (reported beside the
+    algorithmic count, never in place of it)."""
+    m, n = min(rows, cols), max(rows, cols)
+    return steps * (4 * m * m * n + 2 * m ** 3)
+
+
 def bank_bytes(spec) -> dict:
     numel = spec.batch * spec.rows * spec.cols
     g = 4 if spec.grad_dtype == "f32" else 2
@@ -146,6 +153,40 @@ def main():
     ms_per_step = start.elapsed_time(stop) / args.steps
     per_kernel = api.mb_timing_read()
 
+    # ---- spread of single steps: a separate pass, each step between two events of its own (outside
+    # the timed region above, which ms_per_step comes from)
+    n_dist = 20
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_dist + 1)]
+    evs[0].record(stream)
+    for k in range(n_dist):
+        api.muon_bank_step(banks, workspace=ws, stream=stream)
+        evs[k + 1].record(stream)
+    torch.cuda.synchronize()
+    step_ms = np.array([evs[k].elapsed_time(evs[k + 1]) for k in range(n_dist)])
+
+    # ---- the apply alone on the first bank, cold: a 1 GiB buffer is written first so that neither the
+    # L2s nor the 256 MB MALL hold the weights (the in-step apply may find them there)
+    cold = None
+    if banks[0].w_hi.numel() > 0:
+        scrub = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(7)
+        v = (torch.randn(banks[0].w_hi.shape, generator=gen, device="cuda") * 1e-2).to(torch.bfloat16)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        cold_ms = []
+        for k in range(3):
+            scrub.fill_(k + 1)
+            e0.record(stream)
+            api.mp_apply_update(banks[0].w_hi, banks[0].w_lo, v, 1e-3, 1.0 - 1e-4, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cold_ms.append(e0.elapsed_time(e1))
+        del scrub
+        b0 = bank_bytes(specs[0])["apply"]
+        cold = {"bank": specs[0].name, "bytes": b0, "us": round(float(np.median(cold_ms)) * 1e3, 2),
+                "gbps": round(b0 / (float(np.median(cold_ms)) * 1e-3) / 1e9, 1),
+                "note": "median of 3 launches, each after a 1 GiB buffer write"}
+
     live_slots = sum(len(s.live_slots) for s in specs)
     # algorithmic flops by the kernel that does them: banks whose sides are multiples of 256 run
     # all their rounds in the persistent kernel (unless --ns-path 1), the rest one launch per
@@ -158,6 +199,7 @@ def main():
             alg["ns_persist" if persistent else k] += f[k] * len(s.live_slots)
     alg = {k: v for k, v in alg.items() if v > 0}
     ns_flops = sum(alg.values())
+    ns_dense = sum(ns_dense_flops_per_slot(s.rows, s.cols) * len(s.live_slots) for s in specs)
     bytes_ = {"momentum": sum(bank_bytes(s)["momentum"] for s in specs),
               "apply": sum(bank_bytes(s)["apply"] for s in specs)}
 
@@ -202,7 +244,12 @@ def main():
         "ns_ms_per_step": round(ns_ms, 4),
         "ns_tflops": round(ns_flops / (ns_ms * 1e-3) / 1e12, 2) if ns_ms > 0 else None,
         "ns_frac_of_peak": round(ns_flops / (ns_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4) if ns_ms > 0 else None,
+        "ns_dense_equiv_tflops": round(ns_dense / (ns_ms * 1e-3) / 1e12, 2) if ns_ms > 0 else None,
+        "step_ms_distribution": {"steps": n_dist, "p10": round(float(np.percentile(step_ms, 10)), 4),
+                                 "median": round(float(np.median(step_ms)), 4),
+                                 "p90": round(float(np.percentile(step_ms, 90)), 4)},
         "apply_gbps": round(kernels.get("apply", {}).get("gbps", 0.0), 1),
+        "apply_cold": cold,
         "apply_frac_of_hbm": round(kernels.get("apply", {}).get("gbps", 0.0) / PEAK_HBM_GBPS, 4),
         "momentum_gbps": round(kernels.get("momentum", {}).get("gbps", 0.0), 1),
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
@@ -210,6 +257,7 @@ def main():
         "wall_s_timed": round(wall, 4),
         "kernel_timing": {"steps_bracketed": sampled, "every": every},
         "roofline": roofline,
+        "device_fault": api.mb_device_fault(),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"], out["parity"] = cpu_baseline(specs, hosts, sample)
@@ -267,9 +315,12 @@ def cpu_baseline(specs, hosts, sample=None):
     parity = _sample_parity(oracle, specs[0], hosts[0], sample) if sample is not None else None
     try:
         from threadpoolctl import threadpool_info
-        threads = max([t.get("num_threads", 1) for t in threadpool_info() if t.get("user_api") == "blas"] or [1])
+        info = [t for t in threadpool_info() if t.get("user_api") == "blas"]
+        threads = max([t.get("num_threads", 1) for t in info] or [1])
+        blas = ", ".join(sorted({f"{t.get('internal_api')} {t.get('version')}" for t in info})) or None
     except Exception:
         threads = os.cpu_count() or 1
+        blas = None
     budget_s = 12.0
     flops, elapsed, counts = 0, 0.0, {}
     passes = 0
@@ -282,9 +333,29 @@ def cpu_baseline(specs, hosts, sample=None):
             counts[k] = counts.get(k, 0) + v
     desc = [f"{counts[spec.name]} slot-steps over the {len(spec.live_slots)} live slots of {spec.name} "
             f"({spec.rows}x{spec.cols})" for spec in specs if spec.name in counts]
-    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"full oracle step (momentum, fp64 NS5, exact apply), one slot at a time: {'; '.join(desc)}",
-            "seconds": round(elapsed, 2), "host": platform.processor() or platform.machine()}, parity
+    out = {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"full oracle step (momentum, fp64 NS5, exact apply), one slot at a time: {'; '.join(desc)}",
+           "seconds": round(elapsed, 2), "host": platform.processor() or platform.machine(), "blas": blas}
+    # one slot of the first bank with BLAS held to one thread
+    try:
+        from threadpoolctl import threadpool_limits
+        spec, h = specs[0], hosts[0]
+        s = spec.live_slots[0]
+        with threadpool_limits(limits=1, user_api="blas"):
+            t0 = time.perf_counter()
+            _oracle_slot(oracle, spec, h, s)
+            out["single_thread_s_per_slot"] = round(time.perf_counter() - t0, 3)
+    except ImportError:
+        pass
+    return out, parity
+
+
+def _oracle_slot(oracle, spec, h, s):
+    sl = np.ascontiguousarray
+    bf = spec.grad_dtype == "bf16"
+    vals = (lambda a: a.astype(np.float64)) if not bf else oracle.bf16_bits_to_f64
+    oracle.muon_bank_step(vals(sl(h["grad"][s:s + 1])), vals(sl(h["momentum"][s:s + 1])),
+                          sl(h["w_hi"][s:s + 1]), sl(h["w_lo"][s:s + 1]), oracle.F32 if not bf else oracle.BF16)
 
 
 def _oracle_pass(oracle, specs, hosts, budget_s):
@@ -297,12 +368,8 @@ def _oracle_pass(oracle, specs, hosts, budget_s):
             if elapsed >= budget_s:
                 break
             take.append(s)
-            sl = np.ascontiguousarray
-            bf = spec.grad_dtype == "bf16"
-            vals = (lambda a: a.astype(np.float64)) if not bf else oracle.bf16_bits_to_f64
             t0 = time.perf_counter()
-            oracle.muon_bank_step(vals(sl(h["grad"][s:s + 1])), vals(sl(h["momentum"][s:s + 1])),
-                                  sl(h["w_hi"][s:s + 1]), sl(h["w_lo"][s:s + 1]), oracle.F32 if not bf else oracle.BF16)
+            _oracle_slot(oracle, spec, h, s)
             elapsed += time.perf_counter() - t0
             f = ns_flops_per_slot(spec.rows, spec.cols)
             flops += sum(f.values())

@@ -180,6 +180,16 @@ mb_status transpose_add(void *dst, const void *src, int64_t rows, int64_t cols, 
  * already enqueued are not affected. */
 int32_t mb_ns_set_path(int32_t path);
 
+/* Fault flag of the persistent Newton-Schulz launches on the current device.  A
+ * task of that launch waits for the previous contraction of its slot; the wait
+ * gives up after 200 ms (no correct schedule comes near it), the launch then
+ * finishes with undefined values in the affected slots, and this flag is set.
+ * Returns 1 if any launch on the device has set it since it was last cleared, 0
+ * if none has, -1 on a HIP error (detail in mb_last_error()); clears it when
+ * `clear` is nonzero.  Blocking: it reads device memory on the null stream, so
+ * call it after synchronizing the streams the steps were enqueued on. */
+int32_t mb_device_fault(int32_t clear);
+
 /* Kernel timing (off by default).  While enabled, every kernel the library
  * launches is bracketed by two hipEvents on its stream; mb_timing_read waits
  * for them and returns, per kernel name, the launch count and the summed

@@ -59,7 +59,7 @@ _lib = None
 
 EXPORTED = ("mb_default_hparams", "mb_status_string", "mb_last_error", "mb_version", "mb_step_workspace_bytes",
             "mb_ns_workspace_bytes", "muon_bank_step", "muon_momentum_update", "ns_orthogonalize_batched",
-            "ns_orthogonalize_batched_sched", "mp_apply_update", "transpose_copy", "transpose_add", "mb_ns_set_path", "mb_timing_enable", "mb_timing_read")
+            "ns_orthogonalize_batched_sched", "mp_apply_update", "transpose_copy", "transpose_add", "mb_ns_set_path", "mb_device_fault", "mb_timing_enable", "mb_timing_read")
 
 
 def lib() -> ctypes.CDLL:
@@ -85,6 +85,7 @@ def lib() -> ctypes.CDLL:
         "ns_orthogonalize_batched_sched": (i32, [vp, vp, i64, i64, i64, i32, vp, f64, vp, sz, vp]),
         "mp_apply_update": (i32, [vp, vp, vp, i64, i64, f32, f32, vp, vp]),
         "mb_ns_set_path": (i32, [i32]),
+        "mb_device_fault": (i32, [i32]),
         "transpose_copy": (i32, [vp, vp, i64, i64, i32, vp]),
         "transpose_add": (i32, [vp, vp, i64, i64, i32, vp]),
         "mb_timing_enable": (None, [i32]),
@@ -315,6 +316,15 @@ def mb_ns_set_path(path: int) -> int:
     if prev < 0:
         raise ValueError(f"unknown Newton-Schulz path {path}")
     return prev
+
+
+def mb_device_fault(clear: bool = False) -> bool:
+    """Whether a persistent Newton-Schulz launch on the current device gave up a dependency wait at its
+    time cap since the flag was last cleared (blocking; synchronize the step's streams first)."""
+    r = lib().mb_device_fault(1 if clear else 0)
+    if r < 0:
+        raise MuonBankError(8, lib().mb_last_error().decode())
+    return r == 1
 
 
 def mb_timing_enable(on: bool) -> None:

@@ -73,6 +73,9 @@ struct NsPersistBank {
 int ns_persist_tile(int64_t rows, int64_t cols, int steps);
 hipError_t ns_persist(const NsPersistBank* banks, int nbanks, int tile, const NsCoef* coef, int steps, int* sync,
                       hipStream_t stream);
+// The current device's persistent-launch fault flag (1: a dependency wait hit its time cap since the
+// flag was last cleared); blocking; clears it when `clear` is set.
+hipError_t ns_persist_fault(int* flag, bool clear);
 
 // Every Newton-Schulz round of a bank of small slots (Gram side <= 64, <= 4096 elements) in one
 // launch, one workgroup per slot (x0 -> dest; dest may equal x0).

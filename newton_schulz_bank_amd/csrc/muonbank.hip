@@ -652,6 +652,16 @@ int32_t mb_ns_set_path(int32_t path) {
     return g_ns_path.exchange(path);
 }
 
+int32_t mb_device_fault(int32_t clear) {
+    int flag = 0;
+    const hipError_t e = mb::ns_persist_fault(&flag, clear != 0);
+    if (e != hipSuccess) {
+        fail(MB_ERR_HIP, "mb_device_fault: %s", hipGetErrorString(e));
+        return -1;
+    }
+    return flag != 0 ? 1 : 0;
+}
+
 void mb_timing_enable(int32_t on) {
     std::lock_guard<std::mutex> lk(g_timing_mu);
     g_timing_on = on != 0;

@@ -35,6 +35,10 @@
 
 namespace mb {
 
+// Set (never cleared by a kernel) when a dependency wait of any persistent launch on this device hits
+// its time cap; read and cleared from the host through ns_persist_fault.
+__device__ int g_persist_fault;
+
 namespace {
 
 constexpr uint64_t kWaitCapTicks = 20000000;   // 200 ms of the 100 MHz constant clock
@@ -135,6 +139,7 @@ __global__ void __launch_bounds__(C::NT, 2) ns_persist_kernel(PersistArgs p) {
                 if ((spin & 63) == 63 && (__builtin_amdgcn_readfirstlane(ld_relaxed(p.err)) != 0 ||
                                           wall_clock64() - t0 > kWaitCapTicks)) {
                     __hip_atomic_store(p.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(&g_persist_fault, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
                     break;
                 }
             }
@@ -268,6 +273,13 @@ hipError_t device_shape(DeviceShape* out) {
 }
 
 }  // namespace
+
+hipError_t ns_persist_fault(int* flag, bool clear) {
+    hipError_t e = hipMemcpyFromSymbol(flag, HIP_SYMBOL(g_persist_fault), sizeof(int), 0, hipMemcpyDeviceToHost);
+    if (e != hipSuccess || !clear || *flag == 0) return e;
+    const int zero = 0;
+    return hipMemcpyToSymbol(HIP_SYMBOL(g_persist_fault), &zero, sizeof(int), 0, hipMemcpyHostToDevice);
+}
 
 int ns_persist_tile(int64_t rows, int64_t cols, int steps) {
     const int64_t m = rows < cols ? rows : cols, n = rows < cols ? cols : rows;

@@ -35,6 +35,10 @@ def test_flop_count_matches_a_count_of_multiply_adds(m, n):
     f = bench.ns_flops_per_slot(m, n)
     assert sum(f.values()) == 5 * per_round
     assert sum(bench.ns_flops_per_slot(n, m).values()) == 5 * per_round   # tall = wide transposed
+    # the dense-equivalent count takes every product in full: m x m from n (twice: X X^T is computed as
+    # a whole), m x m from m, m x n from m
+    dense = 2 * (m * m * n + m * m * m + m * n * m)
+    assert bench.ns_dense_flops_per_slot(m, n) == bench.ns_dense_flops_per_slot(n, m) == 5 * dense
 
 
 def _oracle_sample(spec, h):

@@ -33,6 +33,14 @@ def _gpu():
     if not torch.cuda.is_available():
         pytest.fail("GPU tests need a GPU")
     api.lib()
+    api.mb_device_fault(clear=True)
+
+
+def assert_no_wait_fault():
+    """No dependency wait of a persistent launch gave up at its time cap (which would leave undefined
+    values in the affected slots)."""
+    torch.cuda.synchronize()
+    assert not api.mb_device_fault(), "a persistent Newton-Schulz launch gave up a dependency wait"
 
 
 # ---------------------------------------------------------------------------
@@ -215,6 +223,7 @@ def test_ns_persistent_bitwise_and_oracle(shape):
     np.testing.assert_array_equal(got, ref)
     if shape[0] >= 3:
         assert np.all(got[1] == 0)
+    assert_no_wait_fault()
     if shape[1] * shape[2] <= 768 * 768:
         err = rel_fro(vals(got), oracle.newton_schulz(vals(x)))
         say(f"  rel err per slot: {np.array2string(err, precision=4)}")
@@ -230,6 +239,7 @@ def test_ns_persistent_steps(steps):
     got = bits(api.ns_orthogonalize_batched(dx, steps=steps))
     torch.cuda.synchronize()
     np.testing.assert_array_equal(got, ref)
+    assert_no_wait_fault()
 
 
 def test_ns_persistent_in_place_and_repeat():
@@ -249,6 +259,7 @@ def test_ns_persistent_in_place_and_repeat():
     torch.cuda.synchronize()
     for o in outs:
         np.testing.assert_array_equal(bits(o), ref)
+    assert_no_wait_fault()
 
 
 # ---------------------------------------------------------------------------

@@ -58,7 +58,10 @@ def _run(config):
 @pytest.mark.parametrize("config", [0, 1, 2, 3, 4])
 def test_bank_step_matches_oracle(config):
     say(f"bank step config {config}")
+    api.mb_device_fault(clear=True)
     specs, host, banks = _run(config)
+    torch.cuda.synchronize()
+    assert not api.mb_device_fault(), "a persistent Newton-Schulz launch gave up a dependency wait"
     samp = SAMPLES[config]
     for bi, (spec, h, b) in enumerate(zip(specs, host, banks)):
         elem = list(range(spec.batch)) if samp["elem"] is None else samp["elem"][bi]
