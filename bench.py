@@ -164,8 +164,10 @@ def main():
     torch.cuda.synchronize()
     step_ms = np.array([evs[k].elapsed_time(evs[k + 1]) for k in range(n_dist)])
 
-    # ---- the apply alone on the first bank, cold: a 1 GiB buffer is written first so that neither the
-    # L2s nor the 256 MB MALL hold the weights (the in-step apply may find them there)
+    # ---- the apply alone on the first bank, cold: a 1 GiB buffer is written (then, separately, read)
+    # first, so that neither the L2s nor the 256 MB MALL hold the weights (the in-step apply may find them
+    # there).  After the write the MALL is full of dirty lines of that buffer, which the apply's own
+    # traffic evicts to HBM; after the read it is clean.
     cold = None
     if banks[0].w_hi.numel() > 0:
         scrub = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -173,19 +175,22 @@ def main():
         gen.manual_seed(7)
         v = (torch.randn(banks[0].w_hi.shape, generator=gen, device="cuda") * 1e-2).to(torch.bfloat16)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        cold_ms = []
-        for k in range(3):
-            scrub.fill_(k + 1)
-            e0.record(stream)
-            api.mp_apply_update(banks[0].w_hi, banks[0].w_lo, v, 1e-3, 1.0 - 1e-4, stream=stream)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            cold_ms.append(e0.elapsed_time(e1))
-        del scrub
         b0 = bank_bytes(specs[0])["apply"]
-        cold = {"bank": specs[0].name, "bytes": b0, "us": round(float(np.median(cold_ms)) * 1e3, 2),
-                "gbps": round(b0 / (float(np.median(cold_ms)) * 1e-3) / 1e9, 1),
-                "note": "median of 3 launches, each after a 1 GiB buffer write"}
+        cold = {"bank": specs[0].name, "bytes": b0, "note": "median of 3 launches, each after a 1 GiB buffer write "
+                "(after_write) or read (after_read)"}
+        for key, prep in (("after_write", lambda k: scrub.fill_(k + 1)),
+                          ("after_read", lambda k: scrub.view(torch.int64).sum())):
+            cold_ms = []
+            for k in range(3):
+                prep(k)
+                e0.record(stream)
+                api.mp_apply_update(banks[0].w_hi, banks[0].w_lo, v, 1e-3, 1.0 - 1e-4, stream=stream)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                cold_ms.append(e0.elapsed_time(e1))
+            med = float(np.median(cold_ms))
+            cold[key] = {"us": round(med * 1e3, 2), "gbps": round(b0 / (med * 1e-3) / 1e9, 1)}
+        del scrub
 
     live_slots = sum(len(s.live_slots) for s in specs)
     # algorithmic flops by the kernel that does them: banks whose sides are multiples of 256 run
