@@ -168,3 +168,18 @@ def test_binding_fails_loudly_without_the_library(monkeypatch):
     monkeypatch.setattr(api, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         api.lib()
+
+
+def test_device_fault_without_a_device_is_an_error(L):
+    """With no GPU the flag cannot be read: -1 and a detail string, never a made-up 0 or 1; the binding
+    raises."""
+    try:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is present: the flag is read for real by the GPU tests")
+    except ImportError:
+        pass
+    assert L.mb_device_fault(0) == -1
+    assert "mb_device_fault" in L.mb_last_error().decode()
+    with pytest.raises(api.MuonBankError):
+        api.mb_device_fault()
