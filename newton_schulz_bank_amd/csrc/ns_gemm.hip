@@ -293,7 +293,7 @@ __global__ void __launch_bounds__(NT, 2) ns_gemm_kernel(GemmArgs args) {
 // Fast path for M, N multiples of the tile and K a multiple of 64 (every bank
 // shape): one workgroup per output tile, the tile body shared with the
 // persistent kernel.  Tile shapes: 128x128 with four wavefronts (two
-// workgroups per CU) or 256x256 with eight (one per CU, twice the flops per
+// workgroups per CU) or 256x256 with sixteen (one per CU, twice the flops per
 // byte moved out of L2).
 // ---------------------------------------------------------------------------
 

@@ -347,7 +347,7 @@ hipError_t ns_persist(const NsPersistBank* banks, int nbanks, int tile, const Ns
         p.coef[t][2] = coef[t].c;
     }
     if (tile == 256) {
-        // one 8-wavefront workgroup per CU (its 128 KiB ring fills the LDS)
+        // one 16-wavefront workgroup per CU (its 128 KiB ring fills the LDS)
         ns_persist_kernel<Cfg256><<<dim3((unsigned)d.cus), Cfg256::NT, 0, stream>>>(p);
     } else {
         // two 4-wavefront workgroups per CU

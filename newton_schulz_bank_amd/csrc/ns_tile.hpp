@@ -40,7 +40,10 @@ struct Cfg {
     static_assert(BM * BN <= RING, "the epilogue staging tile fits the ring");
 };
 using Cfg128 = Cfg<128, 128, 2, 2>;
-using Cfg256 = Cfg<256, 256, 2, 4>;
+// 16 wavefronts of 64x64 (four per SIMD, at most 128 VGPRs each): a third more LDS reads per MFMA
+// than 8 wavefronts of 128x64, but four wavefronts per SIMD cover each other's waits, and the
+// epilogue's LDS round trips and stores are spread over twice the wavefronts.
+using Cfg256 = Cfg<256, 256, 4, 4>;
 
 // K-major tile [rows][8 chunks of 8 k]: chunk c of row R sits at entry R*8 + (c ^ ks(R)),
 // conflict-free for the 16 lanes a 16-byte read serves per cycle.
@@ -319,7 +322,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, lds_u16* smem, int 
     }
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
-#pragma unroll 4
+#pragma unroll
     for (int v = tid; v < CH; v += C::NT) {
         const int i = v / CPRO, c = v % CPRO;
         *reinterpret_cast<u32x4*>(jb.out + (int64_t)(i0 + i) * jb.ldo + j0 + c * 8) =
@@ -333,7 +336,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, lds_u16* smem, int 
         constexpr int UNITS = (C::BM / 32) * (C::BN / 16);
         static_assert(UNITS % C::NW == 0, "transposed units split evenly over the wavefronts");
         const int grp = lane >> 4, t16 = lane & 15, s4 = t16 >> 2, q4 = t16 & 3;
-#pragma unroll 4
+#pragma unroll
         for (int u = wave; u < UNITS; u += C::NW) {
             const int ib = u % (C::BM / 32), jb16 = u / (C::BM / 32);
             const int i = ib * 32 + grp * 8;
