@@ -234,7 +234,11 @@ __global__ void __launch_bounds__(256) apply_kernel(uint16_t* __restrict__ w_hi,
 // host-side launchers
 // ---------------------------------------------------------------------------
 
-int64_t stream_chunk_elems(bool vec) { return vec ? 16384 : 4096; }
+// Elements per workgroup of the streaming kernels (and per partial sum of u^2): 4096 is two 8-element
+// groups per thread, so that enough short workgroups are in flight to overlap the momentum's binary64
+// arithmetic with its memory traffic (16384 per workgroup measured 9 % slower for momentum, 4 % for
+// the apply).
+int64_t stream_chunk_elems(bool) { return 4096; }
 
 int stream_chunks(int64_t slot_numel, bool vec) {
     // fixed chunks of stream_chunk_elems() elements (a multiple of 8), so every
