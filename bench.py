@@ -73,7 +73,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the bank step is measured on a single MI355X; "
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the bank step is measured on a single MI355X; "
                           "--gpus must be 1"}), flush=True)
         sys.exit(2)
 

@@ -1,7 +1,7 @@
 """Build libmuonbank.so (HIP for gfx950) in-tree.
 
 Every source is compiled with hipcc for gfx950 only; the shared library lands
-next to this file so that the binding (and a GPU machine that receives the tree)
+next to this file so that the binding (and any machine that receives a copy of the tree)
 finds it without any install step.
 """
 

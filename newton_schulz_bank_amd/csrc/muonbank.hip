@@ -531,7 +531,7 @@ mb_status muon_bank_step(const mb_bank* banks, int32_t num_banks, const mb_hpara
         char* bw = ws + off;
         off += L.total;
         r.u = b.u_out ? b.u_out : (uint16_t*)(bw + L.u);
-        r.v = b.v_out ? b.v_out : (uint16_t*)(bw + L.u);    // u is dead once round 1 read it
+        r.v = b.v_out ? b.v_out : (uint16_t*)(bw + L.u);    // u is dead once the first round read it
         r.x1 = (uint16_t*)(bw + L.x1);
         r.x2 = (uint16_t*)(bw + L.x2);
         r.A = (uint16_t*)(bw + L.A);
