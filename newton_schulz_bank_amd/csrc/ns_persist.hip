@@ -284,7 +284,9 @@ hipError_t ns_persist_fault(int* flag, bool clear) {
 int ns_persist_tile(int64_t rows, int64_t cols, int steps) {
     const int64_t m = rows < cols ? rows : cols, n = rows < cols ? cols : rows;
     if (steps < 1 || steps > kMaxRounds || m * n > ((int64_t)1 << 30) || m * m > ((int64_t)1 << 30)) return 0;
-    if (m % 256 == 0 && n % 256 == 0) return 256;
+    // a 256-sided Gram is a single 256-tile, so each contraction would be one task per slot: 128-tiles
+    // give four (three for the symmetric ones) and a chain of shorter tasks (workload 0: -24 % per step)
+    if (m % 256 == 0 && n % 256 == 0 && m >= 512) return 256;
     if (m % 128 == 0 && n % 128 == 0) return 128;
     return 0;
 }
