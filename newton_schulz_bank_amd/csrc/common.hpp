@@ -74,22 +74,8 @@ __device__ __forceinline__ double sum_round_odd(double a, double b) {
 // exact value).
 __device__ __forceinline__ float odd53_to_f32(double s) { return (float)s; }
 
-// Round a binary64 value that is round-to-odd at 53 bits to bf16 bits, round
-// to nearest even: first round-to-odd to float32 (24 >= 8 + 2), then RNE to bf16.
-__device__ __forceinline__ uint16_t odd53_to_bf16(double s) {
-    float f = (float)s;
-    if ((double)f != s) {
-        uint32_t b = __float_as_uint(f);
-        if ((b & 1u) == 0u) {
-            b += (fabs(s) > fabs((double)f)) ? 1u : 0xFFFFFFFFu;
-            f = __uint_as_float(b);
-        }
-    }
-    return f32_to_bf16_rne(f);
-}
-
-// RN_bf16 of the exact sum a + b of two binary64 values (correct rounding, ties to even), the
-// same value as odd53_to_bf16(sum_round_odd(a, b)) at a fraction of the cost.  With s = RN53(a + b)
+// RN_bf16 of the exact sum a + b of two binary64 values (correct rounding, ties to even), without
+// a round-to-odd pass through binary64 and float32.  With s = RN53(a + b)
 // and f = RN32(s): a bf16 rounding boundary strictly between the exact sum and s, or between s
 // and f, would be a representable value closer than the one rounded to, so RN_bf16(f) is the
 // answer unless f is a bf16 midpoint.  Then the side of f the exact sum lies on decides: the
