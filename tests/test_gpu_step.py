@@ -137,3 +137,34 @@ def test_per_slot_lr_and_multipliers():
     np.testing.assert_array_equal(bits(b.w_lo), want_lo)
     want_buf, _ = oracle.momentum_nesterov(vals(h["grad"]), vals(h["momentum"]), sc.mu, sc.nu, oracle.BF16)
     np.testing.assert_array_equal(vals(bits(b.momentum)), want_buf)
+
+
+def _fresh_bank(config, index):
+    h = make_bank(config, index)
+    bf = CONFIGS[config][index].grad_dtype == "bf16"
+    b = api.Bank(grad=to_dev(h["grad"], bf), momentum=to_dev(h["momentum"], bf), w_hi=to_dev(h["w_hi"]),
+                 w_lo=to_dev(h["w_lo"]))
+    b.v_out = torch.empty(h["w_hi"].shape, dtype=torch.int16, device="cuda")
+    return b
+
+
+def test_steps_on_two_streams_at_once_match_one_after_the_other():
+    """Two banks stepped concurrently on two streams (default priority), each with its own workspace,
+    give the bits of the same steps run one after the other on the null stream: the persistent
+    launches share no state, and each one's tasks wait only for tasks of the same launch."""
+    say("two streams")
+    seq = [_fresh_bank(1, 0), _fresh_bank(2, 0)]
+    for b in seq:
+        api.muon_bank_step([b])
+    torch.cuda.synchronize()
+    con = [_fresh_bank(1, 0), _fresh_bank(2, 0)]
+    wss = [torch.empty(api.mb_step_workspace_bytes([b]), dtype=torch.uint8, device="cuda") for b in con]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for b, ws, st in zip(con, wss, streams):
+        api.muon_bank_step([b], workspace=ws, stream=st)
+    torch.cuda.synchronize()
+    assert not api.mb_device_fault(), "a persistent Newton-Schulz launch gave up a dependency wait"
+    for a, b in zip(seq, con):
+        for x, y in ((a.w_hi, b.w_hi), (a.w_lo, b.w_lo), (a.v_out, b.v_out), (a.momentum, b.momentum)):
+            np.testing.assert_array_equal(bits(x), bits(y))
