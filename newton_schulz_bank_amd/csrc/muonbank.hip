@@ -45,7 +45,7 @@ struct TimedLaunch {
 };
 
 std::mutex g_timing_mu;
-bool g_timing_on = false;
+std::atomic<bool> g_timing_on{false};   // read without the lock by every launch
 std::vector<TimedLaunch> g_timed;
 // Events are pooled: created when timing is switched on (and on demand), handed back by
 // mb_timing_read, so a timed loop records events without creating any.
@@ -69,7 +69,11 @@ struct Timer final : mb::RoundTimer {
         if (!g_timing_on) return;
         cur.name = name;
         if (!take_event(&cur.start)) return;
-        if (!take_event(&cur.stop)) return;
+        if (!take_event(&cur.stop)) {
+            std::lock_guard<std::mutex> lk(g_timing_mu);
+            g_event_pool.push_back(cur.start);
+            return;
+        }
         (void)hipEventRecord(cur.start, stream);
         open = true;
     }
@@ -666,8 +670,8 @@ void mb_timing_enable(int32_t on) {
     std::lock_guard<std::mutex> lk(g_timing_mu);
     g_timing_on = on != 0;
     // refill only when the pool runs low, so that switching timing on between steps creates no events
-    if (g_timing_on && g_event_pool.size() >= kEventPoolInit / 2) return;
-    while (g_timing_on && g_event_pool.size() < kEventPoolInit) {
+    if (on == 0 || g_event_pool.size() >= kEventPoolInit / 2) return;
+    while (g_event_pool.size() < kEventPoolInit) {
         hipEvent_t e;
         if (hipEventCreate(&e) != hipSuccess) break;
         g_event_pool.push_back(e);
