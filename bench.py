@@ -53,7 +53,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--config", type=int, default=1, help="workload id 0..4 (1 = attention bank, the metric's case)")
+    p.add_argument("--config", type=int, default=1, help="workload id 0..6 (1 = attention bank, the metric's case; 5, 6 = one GPU's share of workloads 3, 4 on 8 GPUs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-parity", action="store_true")
     p.add_argument("--time-every", type=int, default=10,

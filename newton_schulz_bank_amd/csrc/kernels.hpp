@@ -58,6 +58,7 @@ constexpr int kMaxRounds = 64;
 // error word ([16]) and one counter per slot ([32, 32 + total slots)), all cleared before the
 // launch (launch_ns_scale does it).
 constexpr int kMaxPersistBanks = 8;
+constexpr int64_t kMinSlots256 = 16;   // slots a persistent launch needs before it takes 256-tiles
 struct NsPersistBank {
     const uint16_t* x0;
     uint16_t* xa;
@@ -69,8 +70,11 @@ struct NsPersistBank {
     const int* live;
     int64_t batch, rows, cols;
 };
-// Tile edge the persistent kernel uses for a slot shape (256 or 128), 0 if it cannot run it.
-int ns_persist_tile(int64_t rows, int64_t cols, int steps);
+// Tile edge the persistent kernel uses for a slot shape (256 or 128), 0 if it cannot run it; `slots` is
+// the number of slots of that launch whose shape would take 256-tiles.
+int ns_persist_tile(int64_t rows, int64_t cols, int steps, int64_t slots);
+// Whether a slot shape may take 256-tiles at all.
+bool ns_persist_fits256(int64_t rows, int64_t cols);
 hipError_t ns_persist(const NsPersistBank* banks, int nbanks, int tile, const NsCoef* coef, int steps, int* sync,
                       hipStream_t stream);
 // The current device's persistent-launch fault flag (1: a dependency wait hit its time cap since the

@@ -197,6 +197,10 @@ struct StepPlan {
 StepPlan plan_step(const mb_bank* banks, int32_t num_banks) {
     StepPlan pl;
     pl.chunk_of.assign((size_t)num_banks, -1);
+    // the slots that could take 256-tiles decide together whether they do
+    int64_t slots256 = 0;
+    for (int32_t i = 0; i < num_banks; ++i)
+        if (mb::ns_persist_fits256(banks[i].rows, banks[i].cols)) slots256 += banks[i].batch;
     for (int tile : {256, 128}) {
         PersistChunk cur{tile, {}, 0, {}};
         int slots = 0;
@@ -210,7 +214,7 @@ StepPlan plan_step(const mb_bank* banks, int32_t num_banks) {
             slots = 0;
         };
         for (int32_t i = 0; i < num_banks; ++i) {
-            if (mb::ns_persist_tile(banks[i].rows, banks[i].cols, 1) != tile) continue;
+            if (mb::ns_persist_tile(banks[i].rows, banks[i].cols, 1, slots256) != tile) continue;
             cur.base.push_back(slots);
             cur.banks.push_back(i);
             slots += (int)banks[i].batch;
@@ -242,7 +246,7 @@ mb_status run_ns(const uint16_t* x_first, uint16_t* dest, uint16_t* x1, uint16_t
                  int64_t batch, int64_t rows, int64_t cols, const std::vector<mb::NsCoef>& coef,
                  const float* scale, const int* live, int* sync, hipStream_t stream, Timer& timer) {
     const int steps = (int)coef.size();
-    const int tile = mb::ns_persist_tile(rows, cols, steps);
+    const int tile = mb::ns_persist_tile(rows, cols, steps, batch);
     if (g_ns_path.load() == 0 && tile != 0 && sync) {
         const mb::NsPersistBank r{x_first, x1, x2, dest, A, Bm, scale, live, batch, rows, cols};
         timer.begin("ns_persist", stream);

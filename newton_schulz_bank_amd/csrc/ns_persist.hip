@@ -281,12 +281,21 @@ hipError_t ns_persist_fault(int* flag, bool clear) {
     return hipMemcpyToSymbol(HIP_SYMBOL(g_persist_fault), &zero, sizeof(int), 0, hipMemcpyHostToDevice);
 }
 
-int ns_persist_tile(int64_t rows, int64_t cols, int steps) {
+bool ns_persist_fits256(int64_t rows, int64_t cols) {
+    const int64_t m = rows < cols ? rows : cols, n = rows < cols ? cols : rows;
+    // a 256-sided Gram is a single 256-tile, so each contraction would be one task per slot: 128-tiles
+    // give four (three for the symmetric ones) and a chain of shorter tasks (four 256^2 slots: -24 % per step)
+    return m % 256 == 0 && n % 256 == 0 && m >= 512;
+}
+
+int ns_persist_tile(int64_t rows, int64_t cols, int steps, int64_t slots) {
     const int64_t m = rows < cols ? rows : cols, n = rows < cols ? cols : rows;
     if (steps < 1 || steps > kMaxRounds || m * n > ((int64_t)1 << 30) || m * m > ((int64_t)1 << 30)) return 0;
-    // a 256-sided Gram is a single 256-tile, so each contraction would be one task per slot: 128-tiles
-    // give four (three for the symmetric ones) and a chain of shorter tasks (workload 0: -24 % per step)
-    if (m % 256 == 0 && n % 256 == 0 && m >= 512) return 256;
+    // 256-tiles need at least two slots per XCD (8 on gfx950): with fewer, one slot's chain of 256-tile
+    // tasks (six to nine per contraction for an XCD's 32 CUs) sets the launch time, and 128-tiles, four
+    // times as many tasks of a quarter of the work, shorten it (attention (5,768,768) + MLP (3,3072,768):
+    // -15 %; with 21 slots of 1024 x 1024, 4096 x 1024 and 2816 x 768, 256-tiles are 22 % faster)
+    if (ns_persist_fits256(rows, cols) && slots >= kMinSlots256) return 256;
     if (m % 128 == 0 && n % 128 == 0) return 128;
     return 0;
 }

@@ -16,7 +16,11 @@ transposed LM head", section 1.1):
 * the 350M-scale banks (24, 4096, 1024) -> (96, 1024, 1024) and
   (24, 2, 4096, 1024) -> (48, 4096, 1024);
 * the gate matrices smear_gate (1 live of 16) and attn_gate (10 live of 16)
-  ("Muon Custom Sizing", section 2.1 counts their padding).
+  ("Muon Custom Sizing", section 2.1 counts their padding);
+* one rank's share of the big banks when the slot axis is split over 8 GPUs
+  (5 attention and 3 MLP slots per GPU at 124M, "Unified zero-copy optimizer
+  and transposed LM head", section 1.1; 12 + 6 + 3 slots at 350M): the
+  kernels at the shape one GPU of that schedule runs.
 
 Distributions: N(0, s) means standard deviation s, drawn in float64, rounded
 to float32 and then (for bf16 tensors) to bf16, both round-to-nearest-even.
@@ -74,6 +78,11 @@ CONFIGS: dict[int, list[BankSpec]] = {
     4: [BankSpec("attn_1024", 96, 1024, 1024, grad_dist="student_t3"),
         BankSpec("mlp_4096", 48, 4096, 1024, grad_dist="student_t3"),
         BankSpec("mlp_2816", 24, 2816, 768, grad_dist="student_t3", dead_slots=(14, 15))],
+    # one rank's slots of the 124M and of the 350M banks on 8 GPUs (rank 0: every slot live)
+    5: [_attn(batch=5), BankSpec("mlp_3072", 3, 3072, 768)],
+    6: [BankSpec("attn_1024", 12, 1024, 1024, grad_dist="student_t3"),
+        BankSpec("mlp_4096", 6, 4096, 1024, grad_dist="student_t3"),
+        BankSpec("mlp_2816", 3, 2816, 768, grad_dist="student_t3")],
 }
 
 CONFIG_NAMES = {
@@ -82,6 +91,8 @@ CONFIG_NAMES = {
     2: "MLP bank (12,2,3072,768) viewed (24,3072,768), slot 23 dead",
     3: "124M optimizer step: attn (40,768,768) + MLP (24,3072,768) + gates (16,1,12), (16,6,12)",
     4: "350M banks (96,1024,1024) + (48,4096,1024) + (24,2816,768) slots 14-15 dead",
+    5: "one GPU's share of the 124M banks on 8 GPUs: attn (5,768,768) + MLP (3,3072,768)",
+    6: "one GPU's share of the 350M banks on 8 GPUs: (12,1024,1024) + (6,4096,1024) + (3,2816,768)",
 }
 
 

@@ -30,6 +30,8 @@ SAMPLES = {
     2: {"elem": None, "ns": {0: [0, 22]}},
     3: {"elem": None, "ns": {0: [5], 1: [11], 2: [0], 3: [0, 9]}},
     4: {"elem": {0: [0, 95], 1: [0, 47], 2: [0, 13, 14, 15, 23]}, "ns": {0: [50], 1: [7], 2: [13]}},
+    5: {"elem": None, "ns": {0: [0, 4], 1: [0, 2]}},
+    6: {"elem": None, "ns": {0: [11], 1: [5], 2: [0, 2]}},
 }
 
 
@@ -55,7 +57,7 @@ def _run(config):
     return specs, host, banks
 
 
-@pytest.mark.parametrize("config", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("config", [0, 1, 2, 3, 4, 5, 6])
 def test_bank_step_matches_oracle(config):
     say(f"bank step config {config}")
     api.mb_device_fault(clear=True)
