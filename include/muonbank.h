@@ -171,8 +171,8 @@ mb_status transpose_add(void *dst, const void *src, int64_t rows, int64_t cols, 
 /* How stage 2 is scheduled (process-wide; the arithmetic is the same either way).
  *   0 (default): when both sides of a slot are multiples of 128, every round of a
  *     bank runs in one persistent launch: the output tiles (256x256 when both sides
- *     are multiples of 256, the short side is at least 512 and the launch holds at
- *     least 16 such slots, else 128x128) of all
+ *     are multiples of 256, the short side is at least 512 and the launch holds
+ *     more than 8 such slots, else 128x128) of all
  *     three contractions of all rounds are tasks in per-XCD queues, and a task starts
  *     as soon as the previous contraction of its own slot has finished.  Each slot's
  *     tasks run on one XCD (slot s on XCD s % number of XCDs), so its intermediate

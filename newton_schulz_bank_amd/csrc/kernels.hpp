@@ -58,7 +58,7 @@ constexpr int kMaxRounds = 64;
 // error word ([16]) and one counter per slot ([32, 32 + total slots)), all cleared before the
 // launch (launch_ns_scale does it).
 constexpr int kMaxPersistBanks = 8;
-constexpr int64_t kMinSlots256 = 16;   // slots a persistent launch needs before it takes 256-tiles
+constexpr int64_t kMinSlots256 = 9;    // slots a persistent launch needs before it takes 256-tiles
 struct NsPersistBank {
     const uint16_t* x0;
     uint16_t* xa;

@@ -291,10 +291,10 @@ bool ns_persist_fits256(int64_t rows, int64_t cols) {
 int ns_persist_tile(int64_t rows, int64_t cols, int steps, int64_t slots) {
     const int64_t m = rows < cols ? rows : cols, n = rows < cols ? cols : rows;
     if (steps < 1 || steps > kMaxRounds || m * n > ((int64_t)1 << 30) || m * m > ((int64_t)1 << 30)) return 0;
-    // 256-tiles need at least two slots per XCD (8 on gfx950): with fewer, one slot's chain of 256-tile
+    // 256-tiles need more than one slot per XCD (8 on gfx950): with one or none, a slot's chain of 256-tile
     // tasks (six to nine per contraction for an XCD's 32 CUs) sets the launch time, and 128-tiles, four
-    // times as many tasks of a quarter of the work, shorten it (attention (5,768,768) + MLP (3,3072,768):
-    // -15 %; with 21 slots of 1024 x 1024, 4096 x 1024 and 2816 x 768, 256-tiles are 22 % faster)
+    // times as many tasks of a quarter of the work, shorten it (8 slots of 768^2, 3072 x 768, 1024^2:
+    // -13 %, -14 %, -5 %; from 10 slots on 256-tiles are faster on all three, 768^2: 387 against 423 us)
     if (ns_persist_fits256(rows, cols) && slots >= kMinSlots256) return 256;
     if (m % 128 == 0 && n % 128 == 0) return 128;
     return 0;

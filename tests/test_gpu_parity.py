@@ -198,9 +198,9 @@ def test_ns_transpose_equivariance():
 
 PERSIST_SHAPES = [(8, 256, 256), (3, 256, 256), (17, 256, 256), (9, 256, 512), (5, 512, 256), (2, 768, 768),
                   (1, 256, 1024), (2, 1024, 256), (3, 768, 1280),
-                  # sides multiples of 256, short side >= 512 and at least 16 slots: 256x256 tiles (fewer
-                  # slots take 128x128 tiles)
-                  (16, 512, 512), (17, 512, 768), (16, 1024, 512),
+                  # sides multiples of 256, short side >= 512 and more than 8 slots: 256x256 tiles (8 or
+                  # fewer slots take 128x128 tiles, as the shapes above and (8, 512, 512) do)
+                  (9, 512, 512), (8, 512, 512), (16, 512, 512), (17, 512, 768), (16, 1024, 512),
                   # sides multiples of 128 but not of 256: 128x128 tiles, two workgroups per CU
                   (6, 384, 384), (9, 128, 128), (3, 128, 640), (2, 640, 384)]
 
