@@ -361,8 +361,17 @@ hipError_t ns_persist(const NsPersistBank* banks, int nbanks, int tile, const Ns
         // one 16-wavefront workgroup per CU (its 128 KiB ring fills the LDS)
         ns_persist_kernel<Cfg256><<<dim3((unsigned)d.cus), Cfg256::NT, 0, stream>>>(p);
     } else {
-        // two 4-wavefront workgroups per CU
-        ns_persist_kernel<Cfg128><<<dim3((unsigned)(2 * d.cus)), Cfg128::NT, 0, stream>>>(p);
+        int nmax = 0;
+        for (int b = 0; b < nbanks; ++b) nmax = p.bank[b].n > nmax ? p.bank[b].n : nmax;
+        if (nmax <= 768) {
+            // short contractions: one 16-wavefront workgroup per CU finishes each task sooner (four
+            // 256^2 slots -16 %, six 384^2 -20 %, five 768^2 -2 %; all bit-identical)
+            ns_persist_kernel<Cfg128w16><<<dim3((unsigned)d.cus), Cfg128w16::NT, 0, stream>>>(p);
+        } else {
+            // two 4-wavefront workgroups per CU (three 3072 x 768 slots: 9 % faster than 16 wavefronts,
+            // eight 1024^2: 15 %)
+            ns_persist_kernel<Cfg128><<<dim3((unsigned)(2 * d.cus)), Cfg128::NT, 0, stream>>>(p);
+        }
     }
     return hipGetLastError();
 }

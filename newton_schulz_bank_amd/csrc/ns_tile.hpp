@@ -40,6 +40,10 @@ struct Cfg {
     static_assert(BM * BN <= RING, "the epilogue staging tile fits the ring");
 };
 using Cfg128 = Cfg<128, 128, 2, 2>;
+// 16 wavefronts of 32x32 on a 128x128 tile: twice the LDS reads per MFMA of 64x64 wave tiles, but a
+// task finishes about four times sooner on one CU, which is what a chain of short contractions
+// (slots whose long side is at most 768) waits for.
+using Cfg128w16 = Cfg<128, 128, 4, 4>;
 // 16 wavefronts of 64x64 (four per SIMD, at most 128 VGPRs each): a third more LDS reads per MFMA
 // than 8 wavefronts of 128x64, but four wavefronts per SIMD cover each other's waits, and the
 // epilogue's LDS round trips and stores are spread over twice the wavefronts.
