@@ -126,6 +126,18 @@ def _dense(t: torch.Tensor, name: str, elem_size: int | tuple = 2) -> None:
         raise ValueError(f"{name} must have {sizes}-byte elements")
 
 
+def _per_slot(t: torch.Tensor, batch: int, like: torch.Tensor, name: str = "lr_mul_per_slot") -> None:
+    """A per-slot float32 vector: dense, float32, exactly ``batch`` elements, on ``like``'s device (the
+    C ABI reads ``batch`` floats from the pointer and cannot check any of this itself)."""
+    _dense(t, name, 4)
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32 (got {t.dtype})")
+    if t.numel() != batch:
+        raise ValueError(f"{name} must have {batch} elements, one per slot (got {t.numel()})")
+    if t.device != like.device:
+        raise ValueError(f"{name} must be on {like.device} (got {t.device})")
+
+
 def default_hparams() -> mb_hparams:
     hp = mb_hparams()
     lib().mb_default_hparams(ctypes.byref(hp))
@@ -191,9 +203,7 @@ class Bank:
             if tuple(t.shape) != tuple(g.shape):
                 raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(g.shape)}")
         if self.lr_mul_per_slot is not None:
-            _dense(self.lr_mul_per_slot, "lr_mul_per_slot", 4)
-            if self.lr_mul_per_slot.dtype != torch.float32 or self.lr_mul_per_slot.numel() != g.shape[0]:
-                raise ValueError("lr_mul_per_slot must be float32 [batch]")
+            _per_slot(self.lr_mul_per_slot, g.shape[0], g)
         b, r, c = g.shape
         return mb_bank(b, r, c, dt, float(self.lr_mul), float(self.wd_mul), _ptr(g), _ptr(self.momentum),
                        _ptr(self.w_hi), _ptr(self.w_lo), _ptr(self.lr_mul_per_slot), _ptr(self.v_out),
@@ -283,7 +293,7 @@ def mp_apply_update(w_hi: torch.Tensor, w_lo: torch.Tensor, v: torch.Tensor, eff
     batch = w_hi.shape[0] if w_hi.dim() > 1 else 1
     slot = w_hi.numel() // max(batch, 1)
     if lr_mul_per_slot is not None:
-        _dense(lr_mul_per_slot, "lr_mul_per_slot", 4)
+        _per_slot(lr_mul_per_slot, batch, w_hi)
     _check(lib().mp_apply_update(_ptr(w_hi), _ptr(w_lo), _ptr(v), batch, slot, float(eff_lr), float(decay),
                                  _ptr(lr_mul_per_slot), _stream(stream)))
 

@@ -183,3 +183,39 @@ def test_device_fault_without_a_device_is_an_error(L):
     assert "mb_device_fault" in L.mb_last_error().decode()
     with pytest.raises(api.MuonBankError):
         api.mb_device_fault()
+
+
+class _NoCalls:
+    """Stands in for the library: any attribute access means a call was about to be made."""
+
+    def __getattr__(self, name):
+        raise AssertionError(f"the binding reached the library ({name}) with an invalid argument")
+
+
+def test_binding_rejects_a_bad_per_slot_vector_before_any_call(monkeypatch):
+    """mp_apply_update and Bank check lr_mul_per_slot (float32, one element per slot) before anything
+    reaches the C ABI, which would read `batch` floats from the pointer.  Run with host tensors: the
+    device-residency half of the check is relaxed so that the size and dtype halves are what reject."""
+    import torch
+
+    def host_dense(t, name, elem_size=2):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        sizes = elem_size if isinstance(elem_size, tuple) else (elem_size,)
+        if t.element_size() not in sizes:
+            raise ValueError(f"{name} must have {sizes}-byte elements")
+
+    monkeypatch.setattr(api, "_dense", host_dense)
+    monkeypatch.setattr(api, "lib", lambda: _NoCalls())
+    w_hi = torch.zeros((4, 8, 8), dtype=torch.int16)
+    w_lo = torch.zeros_like(w_hi)
+    v = torch.zeros_like(w_hi)
+    with pytest.raises(ValueError, match="4 elements"):
+        api.mp_apply_update(w_hi, w_lo, v, 0.02, 0.9998, lr_mul_per_slot=torch.ones(3, dtype=torch.float32))
+    with pytest.raises(ValueError, match="float32"):
+        api.mp_apply_update(w_hi, w_lo, v, 0.02, 0.9998, lr_mul_per_slot=torch.ones(4, dtype=torch.int32))
+    g = torch.zeros((4, 8, 8), dtype=torch.bfloat16)
+    bank = api.Bank(grad=g, momentum=g.clone(), w_hi=w_hi, w_lo=w_lo, lr_mul_per_slot=torch.ones(5))
+    with pytest.raises(ValueError, match="4 elements"):
+        bank.to_c()
+

@@ -4,8 +4,8 @@ from fractions import Fraction
 
 import numpy as np
 
-from oracle import BF16, F32, bf16_bits_to_f64, muon_bank_step, newton_schulz, recombine, round_fraction, \
-    round_to_bf16, step_scalars
+from oracle import BF16, F32, bf16_bits_to_f64, mp_apply_update, muon_bank_step, newton_schulz, recombine, \
+    round_fraction, round_to_bf16, step_scalars
 from newton_schulz_bank_amd.workloads import CONFIGS, make_bank, make_random_bank
 
 
@@ -63,6 +63,30 @@ def test_per_slot_lr_multiplier():
     np.testing.assert_array_equal(out["w_hi"][0], base["w_hi"][0])
     np.testing.assert_array_equal(out["w_lo"][0], base["w_lo"][0])
     assert out["eta"][1, 0, 0] == base["scalars"].eta * 0.5
+
+
+def test_per_slot_eta_is_one_fp32_multiply():
+    """With a per-slot multiplier m_i the apply uses eta_i = RN32(eta * m_i): one IEEE binary32
+    multiply of the two float32 values.  Multipliers whose product with eta is not a float32 (1.1,
+    1.7, 0.3) pin the rounding: numpy's own float32 multiply gives the expected value, and the
+    weights must be those of the apply with that value, not with the unrounded float64 product."""
+    bank = make_random_bank(9, 4, 8, 8)
+    g = _vals(bank, "grad", "bf16")
+    m = _vals(bank, "momentum", "bf16")
+    per = np.array([1.1, 1.7, 0.3, 1.0], dtype=np.float32)
+    out = muon_bank_step(g, m, bank["w_hi"], bank["w_lo"], BF16, lr_mul_per_slot=per)
+    eta32 = np.float32(out["scalars"].eta)
+    want = np.array([np.float32(eta32 * p) for p in per], dtype=np.float64)
+    np.testing.assert_array_equal(out["eta"][:, 0, 0], want)
+    unrounded = float(eta32) * per.astype(np.float64)
+    assert np.count_nonzero(want != unrounded) >= 3, "these multipliers must give inexact products"
+    hi, lo = mp_apply_update(bank["w_hi"], bank["w_lo"], out["v"], want[:, None, None], out["scalars"].decay)
+    np.testing.assert_array_equal(out["w_hi"], hi)
+    np.testing.assert_array_equal(out["w_lo"], lo)
+    hi_u, lo_u = mp_apply_update(bank["w_hi"], bank["w_lo"], out["v"], unrounded[:, None, None],
+                                 out["scalars"].decay)
+    assert not (np.array_equal(hi_u, out["w_hi"]) and np.array_equal(lo_u, out["w_lo"])), \
+        "the unrounded product must give other weights on this bank"
 
 
 def test_fp32_config_zero_momentum_closed_form():
