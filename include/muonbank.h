@@ -113,7 +113,11 @@ size_t mb_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols);
  *   2. v = NS(u): per slot, on X = u (u^T when rows > cols), X /= ||X||_F + eps,
  *      then ns_steps times A = X X^T, B = b*A + c*A A, X = a*X + B X;
  *      bf16 operands on MFMA with fp32 accumulation; A, B, X rounded to bf16
- *      (round-to-nearest-even) between contractions;
+ *      (round-to-nearest-even) between contractions (slots whose Gram side is
+ *      at most 64, with at most 4096 elements, run on fp32 vector units and
+ *      keep A and B in fp32); ||u||_F is summed in binary64, so a slot is
+ *      skipped (and stays zero) exactly when all its elements are zero, and
+ *      any finite scale of u gives the result of the scaled problem;
  *   3. w = fp32(w_hi << 16 | w_lo); t = RN32(w*decay); r = RN32(t - eta_slot*v)
  *      (one fused multiply-add); w_hi = r >> 16, w_lo = r & 0xFFFF.
  * Banks must not overlap each other.  hp NULL = defaults. */

@@ -100,6 +100,21 @@ __device__ __forceinline__ uint16_t sum_to_bf16(double a, double b) {
     return (uint16_t)h;
 }
 
+// Per-slot live word of the Newton-Schulz kernels: 0 for an all-zero slot; bit 0 for a live slot; bit 1
+// when the first round reads the pre-scaled copy X0 = u * 2^k (k in bits 8 and up, biased) instead of u.
+constexpr int kLiveBit = 1;
+constexpr int kPrescaledBit = 2;
+constexpr int kPrescaleShift = 8;
+constexpr int kPrescaleBias = 512;
+__host__ __device__ __forceinline__ int prescale_exp(int word) { return (word >> kPrescaleShift) - kPrescaleBias; }
+
+// Wavefront (64-lane) sum of doubles with a fixed reduction tree.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
 // Wavefront (64-lane) sum with a fixed reduction tree.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -18,16 +18,19 @@ struct RoundTimer {
 int64_t stream_chunk_elems(bool vec);
 int stream_chunks(int64_t slot_numel, bool vec);
 
-// buf' and u (and, if partials is non-null, per-(slot, chunk) sums of u^2).
-hipError_t launch_momentum(const void* grad, void* buf, uint16_t* u, float* partials, int64_t batch,
+// buf' and u (and, if partials is non-null, per-(slot, chunk) sums of u^2 in binary64).
+hipError_t launch_momentum(const void* grad, void* buf, uint16_t* u, double* partials, int64_t batch,
                            int64_t slot_numel, bool f32, bool vec, float mu, float nu, hipStream_t stream);
-// Per-(slot, chunk) sums of x^2 of a bf16 bank.
-hipError_t launch_sumsq(const uint16_t* x, float* partials, int64_t batch, int64_t slot_numel, bool vec,
+// Per-(slot, chunk) sums of x^2 of a bf16 bank, in binary64.
+hipError_t launch_sumsq(const uint16_t* x, double* partials, int64_t batch, int64_t slot_numel, bool vec,
                         hipStream_t stream);
-// scale[i] = 1 / (sqrt(sum of slot i's partials) + eps); live[i] = (sum > 0).  Also clears, if
-// non-null, heads[0, 32) (queue heads and error word of a persistent launch) and ctr[i].
-hipError_t launch_ns_scale(const float* partials, int nchunks, int64_t batch, float eps, float* scale, int* live,
-                           int* heads, int* ctr, hipStream_t stream);
+// Per slot i, from the sum S of its partials: live[i] = 0 if S == 0 (every element zero), else a live word
+// (common.hpp); scale[i] = 1 / (sqrt(S) + eps), or for a pre-scaled slot 2^-k / (sqrt(S) + eps) with
+// xpre's slot i = x0's slot i * 2^k.  Also clears, if non-null, heads[0, 32) (queue heads, error word and
+// exit count of a persistent launch) and ctr[i].
+hipError_t launch_ns_scale(const double* partials, int nchunks, int64_t batch, double eps, float* scale, int* live,
+                           int* heads, int* ctr, const uint16_t* x0, uint16_t* xpre, int64_t slot_numel,
+                           hipStream_t stream);
 // The mixed-precision apply on [batch, slot_numel].
 hipError_t launch_apply(uint16_t* w_hi, uint16_t* w_lo, const uint16_t* v, int64_t batch, int64_t slot_numel,
                         bool vec, float eta, float decay, const float* lr_mul_per_slot, hipStream_t stream);
@@ -43,8 +46,13 @@ struct NsRound {
     bool first;            // apply the Frobenius scale (x_in is the unscaled input)
     const float* scale;
     const int* live;
+    const uint16_t* x_pre; // first round: pre-scaled slots read X from here instead of x_in
 };
 hipError_t ns_round(const NsRound& r, hipStream_t stream, RoundTimer* timer);
+
+// Where the pre-scaled copy of a slot's first-round input goes (see launch_ns_scale): a ping-pong
+// buffer that the first round neither writes nor, with a single round, has as its output.
+inline uint16_t* ns_prescale_buffer(uint16_t* x1, uint16_t* x2, int steps) { return steps == 1 ? x1 : x2; }
 
 // Coefficients of one Newton-Schulz round, X' = a*X + (b*A + c*A A) X.
 struct NsCoef {
@@ -73,6 +81,9 @@ struct NsPersistBank {
 // Tile edge the persistent kernel uses for a slot shape (256 or 128), 0 if it cannot run it; `slots` is
 // the number of slots of that launch whose shape would take 256-tiles.
 int ns_persist_tile(int64_t rows, int64_t cols, int steps, int64_t slots);
+// Whether the current device's XCD layout allows the persistent launch (else it returns
+// hipErrorNotSupported and callers take one launch per contraction).
+bool ns_persist_supported();
 // Whether a slot shape may take 256-tiles at all.
 bool ns_persist_fits256(int64_t rows, int64_t cols);
 hipError_t ns_persist(const NsPersistBank* banks, int nbanks, int tile, const NsCoef* coef, int steps, int* sync,

@@ -167,7 +167,7 @@ BankWs bank_ws_layout(int64_t batch, int64_t rows, int64_t cols, bool vec) {
     w.x2 = off; off += xb;
     w.A = off; off += ab;
     w.Bm = off; off += ab;
-    w.partials = off; off += round_up((size_t)batch * mb::stream_chunks(rows * cols, vec) * 4);
+    w.partials = off; off += round_up((size_t)batch * mb::stream_chunks(rows * cols, vec) * 8);
     w.scale = off; off += round_up((size_t)batch * 4);
     w.live = off; off += round_up((size_t)batch * 4);
     w.sync = off; off += round_up((size_t)(32 + batch) * 4);
@@ -242,12 +242,16 @@ std::vector<mb::NsCoef> ns_coefs(int steps, double a, double b, double c, const 
     return v;
 }
 
+// Whether this call may use the persistent launch: the process-wide path setting and the device's XCD
+// layout (see mb_ns_set_path).
+bool persist_path() { return g_ns_path.load() == 0 && mb::ns_persist_supported(); }
+
 mb_status run_ns(const uint16_t* x_first, uint16_t* dest, uint16_t* x1, uint16_t* x2, uint16_t* A, uint16_t* Bm,
                  int64_t batch, int64_t rows, int64_t cols, const std::vector<mb::NsCoef>& coef,
                  const float* scale, const int* live, int* sync, hipStream_t stream, Timer& timer) {
     const int steps = (int)coef.size();
     const int tile = mb::ns_persist_tile(rows, cols, steps, batch);
-    if (g_ns_path.load() == 0 && tile != 0 && sync) {
+    if (tile != 0 && sync && persist_path()) {
         const mb::NsPersistBank r{x_first, x1, x2, dest, A, Bm, scale, live, batch, rows, cols};
         timer.begin("ns_persist", stream);
         hipError_t e = mb::ns_persist(&r, 1, tile, coef.data(), steps, sync, stream);
@@ -268,7 +272,8 @@ mb_status run_ns(const uint16_t* x_first, uint16_t* dest, uint16_t* x1, uint16_t
         const bool last = s == steps - 1;
         uint16_t* out = last ? dest : ((s & 1) ? x2 : x1);
         const mb::NsCoef& k = coef[(size_t)s];
-        mb::NsRound r{in, out, A, Bm, batch, rows, cols, k.a, k.b, k.c, s == 0, scale, live};
+        mb::NsRound r{in, out, A, Bm, batch, rows, cols, k.a, k.b, k.c, s == 0, scale, live,
+                      mb::ns_prescale_buffer(x1, x2, steps)};
         hipError_t e = mb::ns_round(r, stream, &timer);
         if (e != hipSuccess) return fail(MB_ERR_HIP, "Newton-Schulz round %d: %s", s, hipGetErrorString(e));
         in = out;
@@ -390,7 +395,7 @@ mb_status ns_orthogonalize_impl(const uint16_t* x, uint16_t* y, int64_t batch, i
 
     hipStream_t st = (hipStream_t)stream;
     char* ws = (char*)workspace;
-    float* partials = (float*)(ws + L.partials);
+    double* partials = (double*)(ws + L.partials);
     float* scale = (float*)(ws + L.scale);
     int* live = (int*)(ws + L.live);
     uint16_t* x1 = (uint16_t*)(ws + L.x1);
@@ -402,8 +407,8 @@ mb_status ns_orthogonalize_impl(const uint16_t* x, uint16_t* y, int64_t batch, i
     if (e != hipSuccess) return fail(MB_ERR_HIP, "sumsq launch: %s", hipGetErrorString(e));
     timer.begin("ns_scale", st);
     int* sync = (int*)(ws + L.sync);
-    e = mb::launch_ns_scale(partials, mb::stream_chunks(rows * cols, vec), batch, f32(eps), scale, live, sync, sync + 32,
-                            st);
+    e = mb::launch_ns_scale(partials, mb::stream_chunks(rows * cols, vec), batch, eps, scale, live, sync, sync + 32, x,
+                            mb::ns_prescale_buffer(x1, x2, steps), rows * cols, st);
     timer.end(st);
     if (e != hipSuccess) return fail(MB_ERR_HIP, "ns_scale launch: %s", hipGetErrorString(e));
     // in place with a single round: write the round to scratch, then copy
@@ -518,13 +523,14 @@ mb_status muon_bank_step(const mb_bank* banks, int32_t num_banks, const mb_hpara
     char* ws = (char*)workspace;
     int* sync = (int*)(ws + banks_bytes);
     const std::vector<mb::NsCoef> coef = ns_coefs(hp.ns_steps, hp.a, hp.b, hp.c, hp.ns_schedule);
-    const bool persist = g_ns_path.load() == 0;
+    const bool persist = persist_path();
     struct Run {
         int64_t slot;
         bool vec;
         int nch;
         uint16_t *u, *v, *x1, *x2, *A, *Bm, *dest;
-        float *partials, *scale;
+        double* partials;
+        float* scale;
         int* live;
     };
     std::vector<Run> runs((size_t)num_banks);
@@ -544,7 +550,7 @@ mb_status muon_bank_step(const mb_bank* banks, int32_t num_banks, const mb_hpara
         r.x2 = (uint16_t*)(bw + L.x2);
         r.A = (uint16_t*)(bw + L.A);
         r.Bm = (uint16_t*)(bw + L.Bm);
-        r.partials = (float*)(bw + L.partials);
+        r.partials = (double*)(bw + L.partials);
         r.scale = (float*)(bw + L.scale);
         r.live = (int*)(bw + L.live);
         // with one round and no v_out, the round would read u while writing v in the same buffer
@@ -573,7 +579,8 @@ mb_status muon_bank_step(const mb_bank* banks, int32_t num_banks, const mb_hpara
             ctr = cs + 32 + c.base[k];
         }
         timer.begin("ns_scale", st);
-        e = mb::launch_ns_scale(r.partials, r.nch, b.batch, f32(hp.eps), r.scale, r.live, heads, ctr, st);
+        e = mb::launch_ns_scale(r.partials, r.nch, b.batch, hp.eps, r.scale, r.live, heads, ctr, r.u,
+                                mb::ns_prescale_buffer(r.x1, r.x2, hp.ns_steps), r.slot, st);
         timer.end(st);
         if (e != hipSuccess) return fail(MB_ERR_HIP, "ns_scale launch: %s", hipGetErrorString(e));
     }

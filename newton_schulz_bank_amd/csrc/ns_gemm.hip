@@ -23,7 +23,9 @@
 //   UPDATE out = sigma*(a*X + acc)    (sigma = s on the first round, else 1)
 // Symmetric outputs are computed on the upper tile triangle only and each
 // off-diagonal tile is also written mirrored.  Slots with a zero norm are
-// skipped; the update writes zeros for them.
+// skipped; the update writes zeros for them.  In the first round a slot whose
+// live word marks it pre-scaled reads X from the pre-scaled copy (the scale
+// then includes the inverse power of two).
 
 #include <cmath>
 
@@ -54,8 +56,15 @@ struct GemmArgs {
     int batch;
     float alpha, beta;          // GRAM: alpha; POLY: c, b; UPDATE: 1, a
     const float* scale;         // per-slot Frobenius scale (first round only), else null
-    const int* live;            // per-slot live flag
+    const int* live;            // per-slot live word
+    const uint16_t* x_in;       // first round: the round's input X (P, Q or aux may be it) ...
+    const uint16_t* x_pre;      // ... and, if non-null, where pre-scaled slots read it instead
 };
+
+// An operand's base for one slot: the pre-scaled copy of X for a pre-scaled slot in the first round.
+__device__ __forceinline__ const uint16_t* slot_base(const GemmArgs& a, const uint16_t* p, int slot) {
+    return (a.x_pre && p == a.x_in && (a.live[slot] & kPrescaledBit)) ? a.x_pre : p;
+}
 
 // Registers staging one 128 (mn) x 64 (k) operand tile: four 16-byte vectors per thread.
 template <bool KMAJOR, bool VEC>
@@ -173,8 +182,8 @@ __global__ void __launch_bounds__(NT, 2) ns_gemm_kernel(GemmArgs args) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE_ELEMS];
     // stage buffer b: P tile at smem + 2*b*TILE_ELEMS, Q tile right after it
 
-    const uint16_t* P = args.P + (int64_t)slot * args.p_stride;
-    const uint16_t* Q = args.Q + (int64_t)slot * args.q_stride;
+    const uint16_t* P = slot_base(args, args.P, slot) + (int64_t)slot * args.p_stride;
+    const uint16_t* Q = slot_base(args, args.Q, slot) + (int64_t)slot * args.q_stride;
 
     Stage<P_KMAJOR, VEC> sp;
     Stage<Q_KMAJOR, VEC> sq;
@@ -229,7 +238,7 @@ __global__ void __launch_bounds__(NT, 2) ns_gemm_kernel(GemmArgs args) {
         const float s = args.scale[slot];
         sig = (EPI == EPI_GRAM) ? s * s : s;
     }
-    const uint16_t* aux = args.aux ? args.aux + (int64_t)slot * args.aux_stride : nullptr;
+    const uint16_t* aux = args.aux ? slot_base(args, args.aux, slot) + (int64_t)slot * args.aux_stride : nullptr;
     const bool mirror = (EPI != EPI_UPDATE) && (ti != tj);
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
@@ -328,10 +337,11 @@ __global__ void __launch_bounds__(C::NT, 2) ns_gemm_fast(GemmArgs args) {
 
     __shared__ __attribute__((aligned(1024))) uint16_t smem[C::RING];
     TileJob jb;
-    jb.P = make_rsrc(args.P + (int64_t)slot * args.p_stride, (uint32_t)(args.p_stride * 2));
-    jb.Q = make_rsrc(args.Q + (int64_t)slot * args.q_stride, (uint32_t)(args.q_stride * 2));
+    jb.P = make_rsrc(slot_base(args, args.P, slot) + (int64_t)slot * args.p_stride, (uint32_t)(args.p_stride * 2));
+    jb.Q = make_rsrc(slot_base(args, args.Q, slot) + (int64_t)slot * args.q_stride, (uint32_t)(args.q_stride * 2));
     jb.X = EPI == EPI_GRAM ? jb.P
-                           : make_rsrc(args.aux + (int64_t)slot * args.aux_stride, (uint32_t)(args.aux_stride * 2));
+                           : make_rsrc(slot_base(args, args.aux, slot) + (int64_t)slot * args.aux_stride,
+                                       (uint32_t)(args.aux_stride * 2));
     jb.ldp = (int)args.ldp;
     jb.ldq = (int)args.ldq;
     jb.ldx = (int)args.ld_aux;
@@ -418,6 +428,8 @@ hipError_t ns_round(const NsRound& r, hipStream_t stream, RoundTimer* timer) {
     g.alpha = 1.f;
     g.scale = r.first ? r.scale : nullptr;
     g.live = r.live;
+    g.x_in = r.x_in;
+    g.x_pre = r.first ? r.x_pre : nullptr;
     if (timer) timer->begin("ns_gram", stream);
     e = tall ? launch_gemm<false, false, EPI_GRAM>(g, (int)r.batch, vec, stream)
              : launch_gemm<true, true, EPI_GRAM>(g, (int)r.batch, vec, stream);
@@ -443,6 +455,8 @@ hipError_t ns_round(const NsRound& r, hipStream_t stream, RoundTimer* timer) {
     GemmArgs u{};
     u.live = r.live;
     u.scale = r.first ? r.scale : nullptr;
+    u.x_in = r.x_in;
+    u.x_pre = r.first ? r.x_pre : nullptr;
     u.alpha = 1.f; u.beta = r.a;
     u.aux = r.x_in; u.aux_stride = slot;
     u.out = r.x_out; u.o_stride = slot;

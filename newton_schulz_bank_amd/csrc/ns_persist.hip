@@ -28,7 +28,9 @@
 // everything a task waits for was claimed earlier by a running workgroup:
 // progress never depends on how many workgroups are resident.  A wait longer
 // than kWaitCapTicks (a fault, never a normal schedule) sets the error word and
-// gives up instead of spinning forever.
+// gives up instead of spinning forever.  The last workgroup to leave checks that
+// every queue was drained (a queue that no workgroup served would leave its
+// tasks undone) and sets the error word otherwise.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "ns_tile.hpp"
@@ -47,6 +49,7 @@ constexpr int kMaxQueues = 16;
 
 struct PersistBank {
     const uint16_t* x0;     // round input of round 0 (unscaled)
+    const uint16_t* xpre;   // round input of round 0 for pre-scaled slots (their live word says which)
     uint16_t* xa;           // outputs of rounds 0, 2, 4, ... (except the last)
     uint16_t* xb;           // outputs of rounds 1, 3, 5, ...
     uint16_t* dest;         // output of the last round
@@ -67,7 +70,8 @@ struct PersistArgs {
     PersistBank bank[kMaxPersistBanks];
     int nbanks, steps, nq;
     int* heads;             // [nq] next task of each queue
-    int* err;               // set when a dependency wait hits its time cap
+    int* err;               // set when a dependency wait hits its time cap or a queue is left undrained
+    int* exits;             // workgroups that have left the task loop
     int* ctr;               // [total slots] tasks finished per slot
     // per queue: tasks of one round, of its Gram block and of its polynomial block, and the
     // number of slots of each bank on the queue
@@ -150,12 +154,13 @@ __global__ void __launch_bounds__(C::NT, 2) ns_persist_kernel(PersistArgs p) {
 
         const bool tall = bk.tall != 0;
         const bool last = t == p.steps - 1;
-        const uint16_t* xin = t == 0 ? bk.x0 : ((t & 1) ? bk.xa : bk.xb);
+        const int lword = bk.live[slot];
+        const bool live = lword != 0;
+        const uint16_t* xin = t == 0 ? ((lword & kPrescaledBit) ? bk.xpre : bk.x0) : ((t & 1) ? bk.xa : bk.xb);
         uint16_t* xout = last ? bk.dest : ((t & 1) ? bk.xb : bk.xa);
         const uint16_t* xs = xin + (int64_t)slot * bk.slot;
         uint16_t* As = bk.A + (int64_t)slot * bk.mm;
         uint16_t* Bs = bk.Bm + (int64_t)slot * bk.mm;
-        const bool live = bk.live[slot] != 0;
         const uint32_t xbytes = (uint32_t)(bk.slot * 2), abytes = (uint32_t)(bk.mm * 2);
 
         TileJob jb;
@@ -248,10 +253,27 @@ __global__ void __launch_bounds__(C::NT, 2) ns_persist_kernel(PersistArgs p) {
         __syncthreads();
         idx = __builtin_amdgcn_readfirstlane(s_task);
     }
+
+    // every claim of this workgroup is made; the last workgroup out checks that each queue's head
+    // passed its task count (claimed tasks always run, so a queue is drained exactly when it did)
+    if (leader) {
+        const int out = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_fetch_add(p.exits, one, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT));
+        if (out == (int)gridDim.x - 1) {
+            bool short_ = false;
+            for (int qq = 0; qq < p.nq; ++qq)
+                short_ |= __builtin_amdgcn_readfirstlane(ld_relaxed(p.heads + qq)) < p.steps * p.per_round[qq];
+            if (short_) {
+                __hip_atomic_store(p.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&g_persist_fault, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            }
+        }
+    }
 }
 
 struct DeviceShape {
     int cus = 0, xccs = 0;
+    bool understood = false;    // one queue per XCD is possible: 1..kMaxQueues XCDs of equal CU count
 };
 
 hipError_t device_shape(DeviceShape* out) {
@@ -264,7 +286,9 @@ hipError_t device_shape(DeviceShape* out) {
         DeviceShape d;
         if ((e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
         if ((e = hipDeviceGetAttribute(&d.xccs, hipDeviceAttributeNumberOfXccs, dev)) != hipSuccess) return e;
-        if (d.xccs < 1 || d.xccs > kMaxQueues || d.cus % d.xccs != 0) d.xccs = 1;
+        // a layout outside this (one queue for several L2s would hand intermediate results between
+        // non-coherent caches) runs the per-contraction path instead
+        d.understood = d.xccs >= 1 && d.xccs <= kMaxQueues && d.cus > 0 && d.cus % d.xccs == 0;
         cached = d;
         cached_dev = dev;
     }
@@ -279,6 +303,11 @@ hipError_t ns_persist_fault(int* flag, bool clear) {
     if (e != hipSuccess || !clear || *flag == 0) return e;
     const int zero = 0;
     return hipMemcpyToSymbol(HIP_SYMBOL(g_persist_fault), &zero, sizeof(int), 0, hipMemcpyHostToDevice);
+}
+
+bool ns_persist_supported() {
+    DeviceShape d;
+    return device_shape(&d) == hipSuccess && d.understood;
 }
 
 bool ns_persist_fits256(int64_t rows, int64_t cols) {
@@ -307,12 +336,14 @@ hipError_t ns_persist(const NsPersistBank* banks, int nbanks, int tile, const Ns
     DeviceShape d;
     hipError_t e = device_shape(&d);
     if (e != hipSuccess) return e;
+    if (!d.understood) return hipErrorNotSupported;
     PersistArgs p{};
     p.nbanks = nbanks;
     p.steps = steps;
     p.nq = d.xccs;
     p.heads = sync;
     p.err = sync + 16;
+    p.exits = sync + 17;
     p.ctr = sync + 32;
     int base = 0;
     for (int b = 0; b < nbanks; ++b) {
@@ -320,6 +351,7 @@ hipError_t ns_persist(const NsPersistBank* banks, int nbanks, int tile, const Ns
         PersistBank& k = p.bank[b];
         k.tall = r.rows > r.cols ? 1 : 0;
         k.x0 = r.x0;
+        k.xpre = ns_prescale_buffer(r.xa, r.xb, steps);
         k.xa = r.xa;
         k.xb = r.xb;
         k.dest = r.dest;

@@ -5,12 +5,14 @@
 // thousand multiply-adds: one launch per contraction would be all launch cost.
 // Here one workgroup holds a slot in LDS and runs every round ("Muon Custom
 // Sizing", section 2.3; Record 7 walkthrough, section 4.2):
-//     A = RN(sig_A * X X^T),  B = RN(c*(A A) + b*A),  X' = RN(sig_X * (a*X + B X))
-// with fp32 accumulation in increasing k and one round-to-nearest-even to bf16
-// after each contraction, the same rounding points as the tiled kernels
-// (sig_A = s^2 and sig_X = s on the first round, s the slot's Frobenius scale,
-// else 1).  Tall slots are loaded transposed (X = G^T) and stored back
-// transposed.  Values stay fp32 in LDS; every stored value is a bf16 value.
+//     A = sig_A * X X^T,  B = c*(A A) + b*A,  X' = RN(sig_X * (a*X + B X))
+// with fp32 accumulation in increasing k (sig_A = s^2 and sig_X = s on the
+// first round, s the slot's Frobenius scale, else 1).  The iterate X is
+// rounded to bf16 (round to nearest even) after every round, as in the tiled
+// kernels; A and B, which here are never MFMA operands, stay fp32: on slots
+// this small their bf16 roundings alone would take the relative error of the
+// result to about 3 % on some inputs.  Tall slots are loaded transposed
+// (X = G^T) and stored back transposed.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -46,16 +48,18 @@ __global__ void __launch_bounds__(kSmallThreads) ns_small_kernel(SmallArgs p) {
     const int tid = threadIdx.x;
     const uint16_t* src = p.x0 + (int64_t)slot * mn;
     uint16_t* dst = p.dest + (int64_t)slot * mn;
-    const bool live = p.live[slot] != 0;
-    if (!live) {
+    const int lword = p.live[slot];
+    if (lword == 0) {
         // a zero slot's result is exactly zero (dest may alias x0: nothing was read)
         for (int e = tid; e < mn; e += kSmallThreads) dst[e] = 0;
         return;
     }
-    // X[i][k] = u[i][k] (wide) or u[k][i] (tall: u is n x m)
+    // X[i][k] = u[i][k] (wide) or u[k][i] (tall: u is n x m); a pre-scaled slot takes X = u * 2^k,
+    // exact in fp32, with the inverse power of two in its scale
+    const int pk = (lword & kPrescaledBit) ? prescale_exp(lword) : 0;
     for (int e = tid; e < mn; e += kSmallThreads) {
         const int i = e / n, k = e - i * n;
-        X[e] = bf16_to_f32(p.tall ? src[(int64_t)k * m + i] : src[e]);
+        X[e] = ldexpf(bf16_to_f32(p.tall ? src[(int64_t)k * m + i] : src[e]), pk);
     }
     const float s = p.scale[slot];
     __syncthreads();
@@ -66,14 +70,14 @@ __global__ void __launch_bounds__(kSmallThreads) ns_small_kernel(SmallArgs p) {
             const int i = e / m, j = e - i * m;
             float acc = 0.f;
             for (int k = 0; k < n; ++k) acc = __fmaf_rn(X[i * n + k], X[j * n + k], acc);
-            A[e] = round_bf16(sig_a * acc);
+            A[e] = sig_a * acc;
         }
         __syncthreads();
         for (int e = tid; e < mm; e += kSmallThreads) {
             const int i = e / m, j = e - i * m;
             float acc = 0.f;
             for (int k = 0; k < m; ++k) acc = __fmaf_rn(A[i * m + k], A[k * m + j], acc);
-            B[e] = round_bf16(__fmaf_rn(b, A[e], c * acc));
+            B[e] = __fmaf_rn(b, A[e], c * acc);
         }
         __syncthreads();
         for (int e = tid; e < mn; e += kSmallThreads) {

@@ -41,16 +41,33 @@ __device__ __forceinline__ void momentum_elem(float g, float b, float mu, float 
     u_val = bf16_to_f32(u_bits);
 }
 
+// Sum of squares of bf16 values in binary64: each square is exact (<= 16 significant bits) and no square
+// of a nonzero bf16 value underflows (the smallest is 2^-266) or overflows, so a slot's sum is zero exactly
+// when every element is zero.
+__device__ __forceinline__ double add_sq(double acc, float v) {
+    const double d = (double)v;
+    return __fma_rn(d, d, acc);
+}
+
+// Fixed-order workgroup sum of 256 threads (wavefront trees, then the four wavefront sums in a fixed
+// order); the result is valid in thread 0.
+__device__ __forceinline__ double block_sum256(double v, double* red) {
+    v = wave_sum_f64(v);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
 template <bool F32, bool VEC>
 __global__ void __launch_bounds__(256) momentum_kernel(const void* __restrict__ grad_, void* __restrict__ buf_,
-                                                       uint16_t* __restrict__ u, float* __restrict__ partials,
+                                                       uint16_t* __restrict__ u, double* __restrict__ partials,
                                                        int64_t slot_numel, int64_t chunk_elems, float mu, float nu) {
     const int64_t slot = blockIdx.y;
     const int64_t chunk = blockIdx.x;
     const int64_t base = slot * slot_numel;
     const int64_t lo = chunk * chunk_elems;
     const int64_t hi = min(lo + chunk_elems, slot_numel);
-    float acc = 0.f;
+    double acc = 0.0;
     if (VEC) {
         // 8 consecutive elements per thread per step; slot_numel % 8 == 0 and bases are 16-byte aligned
         for (int64_t e = lo + (int64_t)threadIdx.x * 8; e < hi; e += 256 * 8) {
@@ -79,7 +96,7 @@ __global__ void __launch_bounds__(256) momentum_kernel(const void* __restrict__ 
             for (int q = 0; q < 8; ++q) {
                 float uv;
                 momentum_elem(g[q], b[q], mu, nu, bn32[q], bn16[q], ub[q], F32, uv);
-                acc = __fmaf_rn(uv, uv, acc);
+                acc = add_sq(acc, uv);
             }
             if (F32) {
                 float4* bp = reinterpret_cast<float4*>((float*)buf_ + idx);
@@ -110,18 +127,15 @@ __global__ void __launch_bounds__(256) momentum_kernel(const void* __restrict__ 
             float bn32, uv;
             uint16_t bn16, ub;
             momentum_elem(g, b, mu, nu, bn32, bn16, ub, F32, uv);
-            acc = __fmaf_rn(uv, uv, acc);
+            acc = add_sq(acc, uv);
             if (F32) ((float*)buf_)[idx] = bn32;
             else ((uint16_t*)buf_)[idx] = bn16;
             u[idx] = ub;
         }
     }
-    // block reduction in a fixed order: wave tree, then wave 0 adds the four wave sums
-    __shared__ float red[4];
-    acc = wave_sum(acc);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
-    __syncthreads();
-    if (threadIdx.x == 0 && partials) partials[slot * gridDim.x + chunk] = (red[0] + red[1]) + (red[2] + red[3]);
+    __shared__ double red[4];
+    acc = block_sum256(acc, red);
+    if (threadIdx.x == 0 && partials) partials[slot * gridDim.x + chunk] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -129,56 +143,94 @@ __global__ void __launch_bounds__(256) momentum_kernel(const void* __restrict__ 
 // ---------------------------------------------------------------------------
 
 template <bool VEC>
-__global__ void __launch_bounds__(256) sumsq_kernel(const uint16_t* __restrict__ x, float* __restrict__ partials,
+__global__ void __launch_bounds__(256) sumsq_kernel(const uint16_t* __restrict__ x, double* __restrict__ partials,
                                                     int64_t slot_numel, int64_t chunk_elems) {
     const int64_t slot = blockIdx.y;
     const int64_t chunk = blockIdx.x;
     const int64_t base = slot * slot_numel;
     const int64_t lo = chunk * chunk_elems;
     const int64_t hi = min(lo + chunk_elems, slot_numel);
-    float acc = 0.f;
+    double acc = 0.0;
     if (VEC) {
         for (int64_t e = lo + (int64_t)threadIdx.x * 8; e < hi; e += 256 * 8) {
             u32x4 v = *reinterpret_cast<const u32x4*>(x + base + e);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                float a = __uint_as_float(v[q] << 16), b = __uint_as_float(v[q] & 0xFFFF0000u);
-                acc = __fmaf_rn(a, a, acc);
-                acc = __fmaf_rn(b, b, acc);
+                acc = add_sq(acc, __uint_as_float(v[q] << 16));
+                acc = add_sq(acc, __uint_as_float(v[q] & 0xFFFF0000u));
             }
         }
     } else {
-        for (int64_t e = lo + threadIdx.x; e < hi; e += 256) {
-            float a = bf16_to_f32(x[base + e]);
-            acc = __fmaf_rn(a, a, acc);
-        }
+        for (int64_t e = lo + threadIdx.x; e < hi; e += 256) acc = add_sq(acc, bf16_to_f32(x[base + e]));
     }
-    __shared__ float red[4];
-    acc = wave_sum(acc);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
-    __syncthreads();
-    if (threadIdx.x == 0) partials[slot * gridDim.x + chunk] = (red[0] + red[1]) + (red[2] + red[3]);
+    __shared__ double red[4];
+    acc = block_sum256(acc, red);
+    if (threadIdx.x == 0) partials[slot * gridDim.x + chunk] = acc;
 }
 
 // ---------------------------------------------------------------------------
-// per-slot scale and live flag: one wavefront per slot, fixed order
+// per-slot scale and live word; pre-scaled copy of slots outside the folded range
 // ---------------------------------------------------------------------------
 
-__global__ void __launch_bounds__(64) ns_scale_kernel(const float* __restrict__ partials, int nchunks, float eps,
-                                                      float* __restrict__ scale, int* __restrict__ live,
-                                                      int* __restrict__ heads, int* __restrict__ ctr) {
+// The Frobenius scale s = 1 / (||u||_F + eps) is folded into the first round (the Gram of the unscaled u
+// times s^2, the update times s).  That is safe while the bf16 products of u stay normal in fp32 and s^2
+// stays finite: ||u||_F in [2^kFoldMinExp, 2^kFoldMaxExp].  A live slot outside that range gets an exact
+// power-of-two copy X0 = u * 2^k with ||X0||_F in [1, 2) (k = -floor(log2 ||u||_F)), which the first round
+// reads instead of u, and scale = 2^-k / (||u||_F + eps), so that scale * X0 = s * u as before.
+constexpr int kFoldMinExp = -45;
+constexpr int kFoldMaxExp = 60;
+constexpr int kScaleParts = 4;          // workgroups per slot (they share the copy of a pre-scaled slot)
+
+__global__ void __launch_bounds__(256) ns_scale_kernel(const double* __restrict__ partials, int nchunks, double eps,
+                                                       float* __restrict__ scale, int* __restrict__ live,
+                                                       int* __restrict__ heads, int* __restrict__ ctr,
+                                                       const uint16_t* __restrict__ x0, uint16_t* __restrict__ xpre,
+                                                       int64_t slot_numel) {
     const int slot = blockIdx.x;
-    // persistent kernel state: queue heads and error word, and this slot's counter
-    if (heads && slot == 0 && threadIdx.x < 32) heads[threadIdx.x] = 0;
-    if (ctr && threadIdx.x == 0) ctr[slot] = 0;
-    float acc = 0.f;
-    for (int i = threadIdx.x; i < nchunks; i += 64) acc += partials[(int64_t)slot * nchunks + i];
-    acc = wave_sum(acc);
-    if (threadIdx.x == 0) {
-        float nrm = sqrtf(acc);
-        scale[slot] = 1.0f / (nrm + eps);
-        live[slot] = acc > 0.f ? 1 : 0;
+    const int part = blockIdx.y;
+    const int tid = threadIdx.x;
+    // persistent kernel state: queue heads, error word and exit count, and this slot's counter
+    if (part == 0) {
+        if (heads && slot == 0 && tid < 32) heads[tid] = 0;
+        if (ctr && tid == 0) ctr[slot] = 0;
     }
+    // every workgroup of the slot forms the same sum in the same order
+    double acc = 0.0;
+    for (int i = tid; i < nchunks; i += 256) acc += partials[(int64_t)slot * nchunks + i];
+    __shared__ double red[4];
+    __shared__ int s_word;
+    acc = block_sum256(acc, red);
+    if (tid == 0) {
+        const double nrm = sqrt(acc);
+        int word = 0;
+        float sc = 0.f;
+        if (acc > 0.0) {
+            const int e = ilogb(nrm);
+            if (e >= kFoldMinExp && e < kFoldMaxExp) {
+                word = kLiveBit;
+                sc = (float)(1.0 / (nrm + eps));
+            } else {
+                const int k = -e;
+                word = kLiveBit | kPrescaledBit | ((k + kPrescaleBias) << kPrescaleShift);
+                sc = (float)(ldexp(1.0, -k) / (nrm + eps));
+            }
+        }
+        s_word = word;
+        if (part == 0) {
+            scale[slot] = sc;
+            live[slot] = word;
+        }
+    }
+    __syncthreads();
+    const int word = s_word;
+    if (!(word & kPrescaledBit)) return;
+    const int k = prescale_exp(word);
+    const uint16_t* src = x0 + (int64_t)slot * slot_numel;
+    uint16_t* dst = xpre + (int64_t)slot * slot_numel;
+    const int64_t per = (slot_numel + kScaleParts - 1) / kScaleParts;
+    const int64_t lo = (int64_t)part * per, hi = min(lo + per, slot_numel);
+    // exact: |X0| < 2, and only elements below 2^-126 of the norm can lose bits
+    for (int64_t e = lo + tid; e < hi; e += 256) dst[e] = f32_to_bf16_rne(ldexpf(bf16_to_f32(src[e]), k));
 }
 
 // ---------------------------------------------------------------------------
@@ -248,7 +300,7 @@ int stream_chunks(int64_t slot_numel, bool vec) {
     return (int)(n < 1 ? 1 : n);
 }
 
-hipError_t launch_momentum(const void* grad, void* buf, uint16_t* u, float* partials, int64_t batch,
+hipError_t launch_momentum(const void* grad, void* buf, uint16_t* u, double* partials, int64_t batch,
                            int64_t slot_numel, bool f32, bool vec, float mu, float nu, hipStream_t stream) {
     const int64_t chunk = stream_chunk_elems(vec);
     dim3 grid((unsigned)stream_chunks(slot_numel, vec), (unsigned)batch);
@@ -262,7 +314,7 @@ hipError_t launch_momentum(const void* grad, void* buf, uint16_t* u, float* part
     return hipGetLastError();
 }
 
-hipError_t launch_sumsq(const uint16_t* x, float* partials, int64_t batch, int64_t slot_numel, bool vec,
+hipError_t launch_sumsq(const uint16_t* x, double* partials, int64_t batch, int64_t slot_numel, bool vec,
                         hipStream_t stream) {
     const int64_t chunk = stream_chunk_elems(vec);
     dim3 grid((unsigned)stream_chunks(slot_numel, vec), (unsigned)batch);
@@ -271,9 +323,11 @@ hipError_t launch_sumsq(const uint16_t* x, float* partials, int64_t batch, int64
     return hipGetLastError();
 }
 
-hipError_t launch_ns_scale(const float* partials, int nchunks, int64_t batch, float eps, float* scale, int* live,
-                           int* heads, int* ctr, hipStream_t stream) {
-    ns_scale_kernel<<<(unsigned)batch, 64, 0, stream>>>(partials, nchunks, eps, scale, live, heads, ctr);
+hipError_t launch_ns_scale(const double* partials, int nchunks, int64_t batch, double eps, float* scale, int* live,
+                           int* heads, int* ctr, const uint16_t* x0, uint16_t* xpre, int64_t slot_numel,
+                           hipStream_t stream) {
+    ns_scale_kernel<<<dim3((unsigned)batch, kScaleParts), 256, 0, stream>>>(partials, nchunks, eps, scale, live, heads,
+                                                                             ctr, x0, xpre, slot_numel);
     return hipGetLastError();
 }
 
