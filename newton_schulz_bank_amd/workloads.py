@@ -12,7 +12,9 @@ transposed LM head", section 1.1):
 * attention QKVO bank (10, 4*768, 768) -> (40, 768, 768);
 * MLP bank (12, 2, 3072, 768) -> (24, 3072, 768), whose last slot is padding;
 * the later MLP bank (12, 2, 2816, 768) -> (24, 2816, 768), with MLP layer 7
-  dead, i.e. view slots 14 and 15;
+  dead, i.e. view slots 14 and 15 (the page counts that slot on the 12-layer
+  index); workload 7 takes the other reading, view slot 7 dead, on the same
+  random draws;
 * the 350M-scale banks (24, 4096, 1024) -> (96, 1024, 1024) and
   (24, 2, 4096, 1024) -> (48, 4096, 1024);
 * the gate matrices smear_gate (1 live of 16) and attn_gate (10 live of 16)
@@ -52,6 +54,7 @@ class BankSpec:
     w_scale: float = 0.02
     lo_uniform: bool = True           # False = zero mantissa
     dead_slots: tuple = field(default_factory=tuple)
+    seed_config: int | None = None    # draw with another workload's seeds (None = this workload's)
 
     @property
     def numel(self) -> int:
@@ -83,6 +86,10 @@ CONFIGS: dict[int, list[BankSpec]] = {
     6: [BankSpec("attn_1024", 12, 1024, 1024, grad_dist="student_t3"),
         BankSpec("mlp_4096", 6, 4096, 1024, grad_dist="student_t3"),
         BankSpec("mlp_2816", 3, 2816, 768, grad_dist="student_t3")],
+    # workload 4 with the other reading of the 2816 bank's dead MLP: view slot 7 (same draws as 4)
+    7: [BankSpec("attn_1024", 96, 1024, 1024, grad_dist="student_t3", seed_config=4),
+        BankSpec("mlp_4096", 48, 4096, 1024, grad_dist="student_t3", seed_config=4),
+        BankSpec("mlp_2816", 24, 2816, 768, grad_dist="student_t3", dead_slots=(7,), seed_config=4)],
 }
 
 CONFIG_NAMES = {
@@ -93,6 +100,7 @@ CONFIG_NAMES = {
     4: "350M banks (96,1024,1024) + (48,4096,1024) + (24,2816,768) slots 14-15 dead",
     5: "one GPU's share of the 124M banks on 8 GPUs: attn (5,768,768) + MLP (3,3072,768)",
     6: "one GPU's share of the 350M banks on 8 GPUs: (12,1024,1024) + (6,4096,1024) + (3,2816,768)",
+    7: "350M banks (96,1024,1024) + (48,4096,1024) + (24,2816,768) view slot 7 dead",
 }
 
 
@@ -130,14 +138,15 @@ def make_bank(config: int, bank: int, spec: BankSpec | None = None, slots=None) 
     keeps only the listed slots of the full draw, for small samples of big banks."""
     spec = spec or CONFIGS[config][bank]
     shape = (spec.batch, spec.rows, spec.cols)
-    g64 = _sample(_rng(config, bank, GRAD), spec.grad_dist, spec.grad_scale, shape)
+    sc = config if spec.seed_config is None else spec.seed_config
+    g64 = _sample(_rng(sc, bank, GRAD), spec.grad_dist, spec.grad_scale, shape)
     if spec.mom_scale is None:
         m64 = np.zeros(shape)
     else:
-        m64 = _rng(config, bank, MOMENTUM).normal(0.0, spec.mom_scale, size=shape)
-    w64 = _rng(config, bank, WEIGHT).normal(0.0, spec.w_scale, size=shape)
+        m64 = _rng(sc, bank, MOMENTUM).normal(0.0, spec.mom_scale, size=shape)
+    w64 = _rng(sc, bank, WEIGHT).normal(0.0, spec.w_scale, size=shape)
     if spec.lo_uniform:
-        lo = _rng(config, bank, MANTISSA).integers(0, 65536, size=shape, dtype=np.uint32).astype(np.uint16)
+        lo = _rng(sc, bank, MANTISSA).integers(0, 65536, size=shape, dtype=np.uint32).astype(np.uint16)
     else:
         lo = np.zeros(shape, dtype=np.uint16)
     if spec.grad_dtype == "f32":
