@@ -139,6 +139,24 @@ mb_status ns_orthogonalize_batched(const uint16_t *x, uint16_t *y,
                                    int32_t steps, double a, double b, double c, double eps,
                                    void *workspace, size_t workspace_bytes, void *stream);
 
+/* Largest scratch ns_orthogonalize_batched_noalloc can use: mb_ns_workspace_bytes of the shape must not
+ * exceed it (the attention bank (40, 768, 768) needs about 236 MB). */
+#define MB_NOALLOC_SCRATCH_BYTES (256u << 20)
+
+/* ns_orthogonalize_batched for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same kernels and results, with the scratch
+ * in a static device array of MB_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs on
+ * until the process ends.  Makes no device allocation and frees nothing; the caller passes x and y as for
+ * ns_orthogonalize_batched (y may equal x).  Shapes whose scratch would exceed the array are rejected with
+ * MB_ERR_WORKSPACE before the device is touched.  Every call on one device shares that device's array:
+ * calls that overlap on one device (other streams, other threads) race and give undefined results;
+ * serialize them.  The array's state from the previous call never matters: whatever must start at zero
+ * is cleared by the call's own kernels. */
+mb_status ns_orthogonalize_batched_noalloc(const uint16_t *x, uint16_t *y,
+                                           int64_t batch, int64_t rows, int64_t cols,
+                                           int32_t steps, double a, double b, double c, double eps,
+                                           void *stream);
+
 /* ns_orthogonalize_batched with per-round coefficients: round t (0-based) uses
  * schedule[3t], schedule[3t+1], schedule[3t+2] as (a, b, c); `schedule` is a
  * host array of 3*steps finite doubles (NULL is MB_ERR_NULL), read during the

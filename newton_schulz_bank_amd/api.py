@@ -59,7 +59,7 @@ _lib = None
 
 EXPORTED = ("mb_default_hparams", "mb_status_string", "mb_last_error", "mb_version", "mb_step_workspace_bytes",
             "mb_ns_workspace_bytes", "muon_bank_step", "muon_momentum_update", "ns_orthogonalize_batched",
-            "ns_orthogonalize_batched_sched", "mp_apply_update", "transpose_copy", "transpose_add", "mb_ns_set_path", "mb_device_fault", "mb_timing_enable", "mb_timing_read")
+            "ns_orthogonalize_batched_sched", "ns_orthogonalize_batched_noalloc", "mp_apply_update", "transpose_copy", "transpose_add", "mb_ns_set_path", "mb_device_fault", "mb_timing_enable", "mb_timing_read")
 
 
 def lib() -> ctypes.CDLL:
@@ -83,6 +83,7 @@ def lib() -> ctypes.CDLL:
         "muon_momentum_update": (i32, [vp, vp, vp, i64, i64, i64, i32, f32, f32, vp]),
         "ns_orthogonalize_batched": (i32, [vp, vp, i64, i64, i64, i32, f64, f64, f64, f64, vp, sz, vp]),
         "ns_orthogonalize_batched_sched": (i32, [vp, vp, i64, i64, i64, i32, vp, f64, vp, sz, vp]),
+        "ns_orthogonalize_batched_noalloc": (i32, [vp, vp, i64, i64, i64, i32, f64, f64, f64, f64, vp]),
         "mp_apply_update": (i32, [vp, vp, vp, i64, i64, f32, f32, vp, vp]),
         "mb_ns_set_path": (i32, [i32]),
         "mb_device_fault": (i32, [i32]),
@@ -280,6 +281,19 @@ def ns_orthogonalize_batched(x: torch.Tensor, y: torch.Tensor | None = None, ste
     _check(lib().ns_orthogonalize_batched(_ptr(x), _ptr(y), bt, r, cc, int(steps), float(a), float(b), float(c),
                                           float(eps), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
     return y
+
+
+def ns_orthogonalize_batched_noalloc(x: torch.Tensor, y: torch.Tensor, steps: int = 5, a: float = 3.4445,
+                                     b: float = -4.7750, c: float = 2.0315, eps: float = 1e-7, stream=None) -> None:
+    """y = NS(x) for bf16 [batch, rows, cols] with the library's static scratch: nothing is allocated here
+    or in the library (y must be given; it may be x)."""
+    _dense(x, "x", 2)
+    _dense(y, "y", 2)
+    if x.dim() != 3 or y.shape != x.shape:
+        raise ValueError("x and y must be [batch, rows, cols] of one shape")
+    bt, r, cc = x.shape
+    _check(lib().ns_orthogonalize_batched_noalloc(_ptr(x), _ptr(y), bt, r, cc, int(steps), float(a), float(b),
+                                                  float(c), float(eps), _stream(stream)))
 
 
 def mp_apply_update(w_hi: torch.Tensor, w_lo: torch.Tensor, v: torch.Tensor, eff_lr: float, decay: float,

@@ -423,9 +423,62 @@ mb_status ns_orthogonalize_impl(const uint16_t* x, uint16_t* y, int64_t batch, i
     return ok();
 }
 
+// ---------------------------------------------------------------------------
+// the allocation-free variant: its scratch is a static device array
+// ---------------------------------------------------------------------------
+
+}  // namespace
+
+// Every device the library runs on holds one copy of this array until the process ends.  Host code
+// never uses its name as an address (on the host that name is a stand-in, not device memory): the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[MB_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (looked up on the first call on that device).
+mb_status scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MB_ERR_HIP, "ns_orthogonalize_batched_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MB_ERR_HIP, "ns_orthogonalize_batched_noalloc: device %d beyond the %d supported", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(MB_ERR_HIP, "ns_orthogonalize_batched_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return MB_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+mb_status ns_orthogonalize_batched_noalloc(const uint16_t* x, uint16_t* y, int64_t batch, int64_t rows, int64_t cols,
+                                           int32_t steps, double a, double b, double c, double eps, void* stream) {
+    // the size check comes first, before anything touches the device
+    if (check_shape(batch, rows, cols, "ns_orthogonalize_batched_noalloc") != MB_OK) return MB_ERR_SHAPE;
+    const size_t need = bank_ws_layout(batch, rows, cols, (rows * cols) % 8 == 0).total;
+    if (need > (size_t)MB_NOALLOC_SCRATCH_BYTES)
+        return fail(MB_ERR_WORKSPACE,
+                    "ns_orthogonalize_batched_noalloc: shape (%lld, %lld, %lld) needs %zu bytes of scratch; the static "
+                    "scratch holds %zu (use ns_orthogonalize_batched with a workspace)",
+                    (long long)batch, (long long)rows, (long long)cols, need, (size_t)MB_NOALLOC_SCRATCH_BYTES);
+    if (!x || !y) return fail(MB_ERR_NULL, "ns_orthogonalize_batched_noalloc: null tensor pointer");
+    void* ws = nullptr;
+    mb_status s = scratch_address(&ws);
+    if (s != MB_OK) return s;
+    return ns_orthogonalize_impl(x, y, batch, rows, cols, steps, a, b, c, nullptr, eps, ws, need, stream);
+}
 
 mb_status ns_orthogonalize_batched(const uint16_t* x, uint16_t* y, int64_t batch, int64_t rows, int64_t cols,
                                    int32_t steps, double a, double b, double c, double eps, void* workspace,

@@ -219,3 +219,13 @@ def test_binding_rejects_a_bad_per_slot_vector_before_any_call(monkeypatch):
     with pytest.raises(ValueError, match="4 elements"):
         bank.to_c()
 
+
+def test_noalloc_rejects_oversized_shapes_before_touching_the_device(L):
+    """The size check of the allocation-free entry point comes before any device call, so it answers
+    without a GPU; shapes within the limit would need the device and are left to the GPU tests."""
+    p = 1 << 36
+    big = (200, 768, 768)
+    assert L.mb_ns_workspace_bytes(*big) > (256 << 20)
+    assert L.ns_orthogonalize_batched_noalloc(p, p + (1 << 30), *big, 5, 3.4445, -4.775, 2.0315, 1e-7, None) == WORKSPACE
+    assert b"static scratch" in L.mb_last_error()
+    assert L.ns_orthogonalize_batched_noalloc(p, p + (1 << 30), 0, 768, 768, 5, 3.4445, -4.775, 2.0315, 1e-7, None) == SHAPE
