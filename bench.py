@@ -1,15 +1,15 @@
 """Benchmark of the Muon bank step on one MI355X.
 
-One step = one full pass of the hot path over the bank: momentum + Nesterov,
-Frobenius pre-scale, five quintic Newton-Schulz rounds (Gram, polynomial,
-update contractions on bf16 MFMA), and the mixed-precision apply.  Inputs
-are seeded synthetic banks (no dataset), resident in HBM before the timed
-region.  The default workload is the attention QKVO bank (10, 3072, 768)
-viewed as (40, 768, 768).
+One step = one full pass of the hot path over every bank of the workload: momentum + Nesterov,
+Frobenius pre-scale, five quintic Newton-Schulz rounds (Gram, polynomial, update contractions on bf16
+MFMA), and the mixed-precision apply.  Inputs are seeded synthetic banks (no dataset), resident in
+HBM before the timed region.  The default workload is the largest that one GPU holds whole: the 350M
+model's banks (96, 1024, 1024) + (48, 4096, 1024) + (24, 2816, 768) with view slots 14-15 dead.
 
-Prints one JSON line.  ``value`` is the step's throughput in algorithmic
-Newton-Schulz TFLOP/s: live slots x 5*(m(m+1)n + m^2(m+1) + 2m^2 n) per
-step (symmetric Gram and A*A counted once) / wall time of the whole step.
+Prints one JSON line.  ``value`` is the step's throughput in algorithmic Newton-Schulz TFLOP/s: live
+slots x 5*(m(m+1)n + m^2(m+1) + 2m^2 n) per step (symmetric Gram and A*A counted once) / wall time of
+the whole step.  The timed region holds the K steps and nothing else; each kernel's average duration
+comes from a separate pass in which every launch is bracketed by events.
 """
 
 from __future__ import annotations
@@ -51,13 +51,17 @@ def bank_bytes(spec) -> dict:
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=100)
-    p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--config", type=int, default=1, help="workload id 0..6 (1 = attention bank, the metric's case; 5, 6 = one GPU's share of workloads 3, 4 on 8 GPUs)")
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", type=int, default=4,
+                   help="workload id 0..7 (4 = the 350M banks, the largest that fits one GPU; 1 = the attention "
+                        "bank; 5, 6 = one GPU's share of workloads 3, 4 on 8 GPUs; 7 = workload 4 with the other "
+                        "dead-slot reading)")
+    p.add_argument("--kernel-steps", type=int, default=10,
+                   help="steps of the separate pass whose kernel launches are each bracketed by events")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-parity", action="store_true")
-    p.add_argument("--time-every", type=int, default=10,
-                   help="bracket the kernels of every N-th timed step with HIP events (1 = every step)")
+    p.add_argument("--no-probes", action="store_true", help="skip the measured-peak probes")
     p.add_argument("--workload", default="bank", choices=("bank", "transpose"),
                    help="bank: the Muon bank step (the headline); transpose: the tied-embedding transposes of "
                         "one optimizer step at the LM-head size")
@@ -123,35 +127,39 @@ def main():
     if not args.no_parity and not args.no_cpu_baseline:
         sample = gpu_sample_step(api, specs[0], hosts[0])
 
-    # ---- timed region: K whole steps back to back, every kernel bracketed by HIP events on the
-    # launch stream (pooled events: nothing is created inside the loop); ms_per_step and the
-    # per-kernel durations come from this same region.  The kernels of every --time-every'th step
-    # are bracketed (each event pair costs the stream a few microseconds, so bracketing every
-    # launch would inflate the step time it is part of); their averages are over those launches.
-    api.mb_timing_enable(True)
+    # ---- timed region: K whole steps back to back between two events on the launch stream, nothing
+    # else inside it
     for _ in range(args.warmup):
         api.muon_bank_step(banks, workspace=ws, stream=stream)
     torch.cuda.synchronize()
-    api.mb_timing_read()
-    api.mb_timing_enable(False)
-    every = max(1, args.time_every)
-    sampled = 0
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record(stream)
     for k in range(args.steps):
-        timed_step = k % every == 0
-        if timed_step:
-            api.mb_timing_enable(True)
-            sampled += 1
         api.muon_bank_step(banks, workspace=ws, stream=stream)
-        if timed_step:
-            api.mb_timing_enable(False)
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = start.elapsed_time(stop) / args.steps
+
+    # ---- per-kernel durations: a separate pass in which every launch is bracketed by the library's
+    # pooled events (created before the pass); one unbracketed step first, so that no bracketed launch
+    # follows a host synchronization
+    api.mb_timing_enable(True)
+    api.mb_timing_read()
+    api.mb_timing_enable(False)
+    api.muon_bank_step(banks, workspace=ws, stream=stream)
+    api.mb_timing_enable(True)
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record(stream)
+    for _ in range(args.kernel_steps):
+        api.muon_bank_step(banks, workspace=ws, stream=stream)
+    k1.record(stream)
+    api.mb_timing_enable(False)
+    torch.cuda.synchronize()
     per_kernel = api.mb_timing_read()
+    sampled = args.kernel_steps
+    kernel_pass_ms = k0.elapsed_time(k1) / args.kernel_steps
 
     # ---- spread of single steps: a separate pass, each step between two events of its own (outside
     # the timed region above, which ms_per_step comes from)
@@ -164,42 +172,45 @@ def main():
     torch.cuda.synchronize()
     step_ms = np.array([evs[k].elapsed_time(evs[k + 1]) for k in range(n_dist)])
 
-    # ---- the apply alone on the first bank, cold: a 1 GiB buffer is written (then, separately, read)
+    # ---- the apply alone on the largest bank, cold: a 1 GiB buffer is written (then, separately, read)
     # first, so that neither the L2s nor the 256 MB MALL hold the weights (the in-step apply may find them
     # there).  After the write the MALL is full of dirty lines of that buffer, which the apply's own
     # traffic evicts to HBM; after the read it is clean.
     cold = None
-    if banks[0].w_hi.numel() > 0:
+    big = max(range(len(specs)), key=lambda i: specs[i].numel)
+    if banks[big].w_hi.numel() > 0:
         scrub = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         gen = torch.Generator(device="cuda")
         gen.manual_seed(7)
-        v = (torch.randn(banks[0].w_hi.shape, generator=gen, device="cuda") * 1e-2).to(torch.bfloat16)
+        v = (torch.randn(banks[big].w_hi.shape, generator=gen, device="cuda") * 1e-2).to(torch.bfloat16)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        b0 = bank_bytes(specs[0])["apply"]
-        cold = {"bank": specs[0].name, "bytes": b0, "note": "median of 3 launches, each after a 1 GiB buffer write "
-                "(after_write) or read (after_read)"}
+        b0 = bank_bytes(specs[big])["apply"]
+        cold = {"bank": specs[big].name, "bytes": b0, "note": "median of 3 launches, each after a 1 GiB buffer "
+                "write (after_write) or read (after_read)"}
         for key, prep in (("after_write", lambda k: scrub.fill_(k + 1)),
                           ("after_read", lambda k: scrub.view(torch.int64).sum())):
             cold_ms = []
             for k in range(3):
                 prep(k)
                 e0.record(stream)
-                api.mp_apply_update(banks[0].w_hi, banks[0].w_lo, v, 1e-3, 1.0 - 1e-4, stream=stream)
+                api.mp_apply_update(banks[big].w_hi, banks[big].w_lo, v, 1e-3, 1.0 - 1e-4, stream=stream)
                 e1.record(stream)
                 torch.cuda.synchronize()
                 cold_ms.append(e0.elapsed_time(e1))
             med = float(np.median(cold_ms))
             cold[key] = {"us": round(med * 1e3, 2), "gbps": round(b0 / (med * 1e-3) / 1e9, 1)}
-        del scrub
+        del scrub, v
+
+    peaks = None if args.no_probes else measure_peaks(torch, stream)
 
     live_slots = sum(len(s.live_slots) for s in specs)
-    # algorithmic flops by the kernel that does them: banks whose sides are multiples of 256 run
-    # all their rounds in the persistent kernel (unless --ns-path 1), the rest one launch per
-    # contraction
+    # algorithmic flops by the kernel that does them: banks whose sides are multiples of 128 run
+    # all their rounds in the persistent kernel (unless --ns-path 1), the rest (gates, ragged shapes)
+    # in the small-slot kernel or one launch per contraction
     alg = {"ns_persist": 0, "ns_gram": 0, "ns_poly": 0, "ns_update": 0}
     for s in specs:
         f = ns_flops_per_slot(s.rows, s.cols)
-        persistent = args.ns_path == 0 and s.rows % 256 == 0 and s.cols % 256 == 0
+        persistent = args.ns_path == 0 and s.rows % 128 == 0 and s.cols % 128 == 0
         for k in ("ns_gram", "ns_poly", "ns_update"):
             alg["ns_persist" if persistent else k] += f[k] * len(s.live_slots)
     alg = {k: v for k, v in alg.items() if v > 0}
@@ -219,14 +230,18 @@ def main():
             kernels[k]["alg_tflops"] = flops_per_launch / (kernels[k]["avg_us"] * 1e-6) / 1e12
     for k in ("momentum", "apply"):
         if k in kernels:
-            b = bytes_[k] / kernels[k]["launches_per_step"]
-            kernels[k]["gbps"] = b / (kernels[k]["avg_us"] * 1e-6) / 1e9
+            kernels[k]["gbps"] = bytes_[k] / (kernels[k]["ms_per_step"] * 1e-3) / 1e9
+            if peaks:
+                kernels[k]["frac_of_measured_copy"] = kernels[k]["gbps"] / peaks["copy_gbps"]
 
     dominant = max(alg, key=lambda k: kernels.get(k, {"ms_per_step": 0})["ms_per_step"])
     achieved = kernels[dominant]["alg_tflops"]
     roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": read_traffic(dominant, args.config)}
+    if peaks:
+        roofline["measured_peak"] = peaks["mfma_bf16_tflops"]
+        roofline["frac_of_measured"] = round(achieved / peaks["mfma_bf16_tflops"], 4)
 
     value = ns_flops / (ms_per_step * 1e-3) / 1e12
     out = {
@@ -257,16 +272,54 @@ def main():
         "apply_cold": cold,
         "apply_frac_of_hbm": round(kernels.get("apply", {}).get("gbps", 0.0) / PEAK_HBM_GBPS, 4),
         "momentum_gbps": round(kernels.get("momentum", {}).get("gbps", 0.0), 1),
+        "momentum_frac_of_hbm": round(kernels.get("momentum", {}).get("gbps", 0.0) / PEAK_HBM_GBPS, 4),
+        "measured_peaks": peaks,
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
         "wall_s_timed": round(wall, 4),
-        "kernel_timing": {"steps_bracketed": sampled, "every": every},
+        "kernel_timing": {"steps_bracketed": sampled, "ms_per_step_bracketed": round(kernel_pass_ms, 4),
+                          "note": "every launch of a separate pass after the timed region bracketed by events"},
         "roofline": roofline,
         "device_fault": api.mb_device_fault(),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"], out["parity"] = cpu_baseline(specs, hosts, sample)
+        # the same whole step's Newton-Schulz work at the oracle's rate
+        out["cpu_baseline"]["s_per_step_equiv"] = round(ns_flops / (out["cpu_baseline"]["value"] * 1e12), 2)
     print(json.dumps(out), flush=True)
+
+
+def measure_peaks(torch, stream):
+    """The measured-peak probes: a register-only bf16 MFMA loop over the whole chip and a 1 GiB device copy
+    in 16-byte vectors (median of 5 launches each, events on the launch stream)."""
+    from newton_schulz_bank_amd import probes
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn, reps=5):
+        fn()
+        out = []
+        for _ in range(reps):
+            ev[0].record(stream)
+            fn()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            out.append(ev[0].elapsed_time(ev[1]))
+        return float(np.median(out))
+    wgs, iters = 256 * 8, 4096
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    ms = timed(lambda: probes.mb_probe_mfma_bf16(iters, wgs, sink, stream=stream))
+    mfma = probes.mfma_flops(iters, wgs) / (ms * 1e-3) / 1e12
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    ms_c = timed(lambda: probes.mb_probe_copy(dst, src, stream=stream))
+    del src, dst, sink
+    return {"mfma_bf16_tflops": round(mfma, 1), "mfma_frac_of_nominal": round(mfma / PEAK_BF16_TFLOPS, 4),
+            "copy_gbps": round(2 * n / (ms_c * 1e-3) / 1e9, 1), "copy_frac_of_nominal":
+            round(2 * n / (ms_c * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "note": "mb_probe_mfma_bf16: 2048 workgroups x 4 wavefronts x 4 independent v_mfma_f32_32x32x16_bf16 "
+                    "chains x 4096 iterations, no memory traffic; mb_probe_copy: 1 GiB device copy, 16-byte vectors "
+                    "(2 GiB of traffic)"}
 
 
 def gpu_sample_step(api, spec, h):
@@ -364,24 +417,23 @@ def _oracle_slot(oracle, spec, h, s):
 
 
 def _oracle_pass(oracle, specs, hosts, budget_s):
-    """One pass over the live slots of every bank, until the budget runs out: (flops, seconds, slots per bank)."""
-    flops, elapsed, counts = 0, 0.0, {}
-    for spec, h in zip(specs, hosts):
-        live = list(spec.live_slots)
-        take = []
-        for s in live:
-            if elapsed >= budget_s:
-                break
-            take.append(s)
-            t0 = time.perf_counter()
-            _oracle_slot(oracle, spec, h, s)
-            elapsed += time.perf_counter() - t0
-            f = ns_flops_per_slot(spec.rows, spec.cols)
-            flops += sum(f.values())
-        counts[spec.name] = len(take)
+    """One pass over the live slots of every bank, taking the banks in turn (one slot of each, then the
+    next slot of each, ...), until the budget runs out: (flops, seconds, slots per bank)."""
+    flops, elapsed, counts = 0, 0.0, {spec.name: 0 for spec in specs}
+    order = []
+    lives = [list(spec.live_slots) for spec in specs]
+    for k in range(max(len(l) for l in lives)):
+        order += [(i, l[k]) for i, l in enumerate(lives) if k < len(l)]
+    for i, s in order:
         if elapsed >= budget_s:
             break
-    return flops, elapsed, counts
+        spec, h = specs[i], hosts[i]
+        t0 = time.perf_counter()
+        _oracle_slot(oracle, spec, h, s)
+        elapsed += time.perf_counter() - t0
+        flops += sum(ns_flops_per_slot(spec.rows, spec.cols).values())
+        counts[spec.name] += 1
+    return flops, elapsed, {k: v for k, v in counts.items() if v}
 
 
 def bench_transpose(args, torch, api):

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmuonbank.so")
-SOURCES = ["muonbank.hip", "stream_kernels.hip", "ns_gemm.hip", "ns_persist.hip", "ns_small.hip", "transpose.hip"]
+SOURCES = ["muonbank.hip", "stream_kernels.hip", "ns_gemm.hip", "ns_persist.hip", "ns_small.hip", "transpose.hip",
+           "probes.hip"]
 BUILD_DIR = os.path.join(HERE, "_build")
 
 FLAGS = [
