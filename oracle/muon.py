@@ -124,9 +124,10 @@ def f64_to_bf16_bits(x) -> np.ndarray:
     return (bits >> np.uint32(16)).astype(np.uint16)
 
 
-def _round_sum_of_products(c1: float, x1, c2: float, x2, fmt: str) -> np.ndarray:
-    """RN_fmt(c1*x1 + c2*x2), correctly rounded, for float32 scalars c1, c2 and
-    arrays x1, x2 of fp32 or bf16 values.
+def _round_sum_of_products(c1, x1, c2, x2, fmt: str) -> np.ndarray:
+    """RN_fmt(c1*x1 + c2*x2), correctly rounded, for float32 coefficients c1, c2
+    (scalars, or arrays that broadcast against x1, e.g. one per slot) and arrays
+    x1, x2 of fp32 or bf16 values.
 
     Each product of two <=24-bit significands is exact in float64; the sum is
     exact unless TwoSum reports a nonzero error, and those few elements are
@@ -134,6 +135,8 @@ def _round_sum_of_products(c1: float, x1, c2: float, x2, fmt: str) -> np.ndarray
     p, emin, emax = _FORMATS[fmt]
     x1 = np.asarray(x1, dtype=np.float64)
     x2 = np.asarray(x2, dtype=np.float64)
+    c1 = np.broadcast_to(np.asarray(c1, dtype=np.float64), x1.shape)
+    c2 = np.broadcast_to(np.asarray(c2, dtype=np.float64), x2.shape)
     p1 = c1 * x1
     p2 = c2 * x2
     s = p1 + p2
@@ -141,7 +144,7 @@ def _round_sum_of_products(c1: float, x1, c2: float, x2, fmt: str) -> np.ndarray
     err = (p1 - (s - bb)) + (p2 - bb)
     out = round_to_format(s, p, emin, emax)
     for idx in zip(*np.nonzero((err != 0) & np.isfinite(s))):
-        q = Fraction(c1) * Fraction(float(x1[idx])) + Fraction(c2) * Fraction(float(x2[idx]))
+        q = Fraction(float(c1[idx])) * Fraction(float(x1[idx])) + Fraction(float(c2[idx])) * Fraction(float(x2[idx]))
         out[idx] = round_fraction(q, p, emin, emax)
     return out
 
@@ -182,11 +185,13 @@ def step_scalars(lr: float, weight_decay: float, momentum: float, rows: int, col
 # momentum and Nesterov update
 # ---------------------------------------------------------------------------
 
-def momentum_nesterov(grad, buf, mu: float, nu: float, storage: str):
+def momentum_nesterov(grad, buf, mu, nu, storage: str):
     """buf' = mu*buf + nu*g  (the buffer's lerp toward g with weight 1-mu), then
     u = nu*g + mu*buf'       (g's lerp toward the *stored* buf' with weight mu)
     ("Muon Custom Sizing", section 4).  buf' is rounded once to the storage
-    format, u once to bf16.  Returns (buf', u) as float64 arrays."""
+    format, u once to bf16.  mu and nu are float32 values, scalars or arrays
+    that broadcast against the bank (one per slot: [batch, 1, 1]).  Returns
+    (buf', u) as float64 arrays."""
     buf_new = _round_sum_of_products(mu, buf, nu, grad, storage)
     u = _round_sum_of_products(nu, grad, mu, buf_new, BF16)
     return buf_new, u
@@ -266,8 +271,8 @@ def split(bits):
 def mp_apply_update(w_hi, w_lo, v, eta, decay: float):
     """w = fp32(hi, lo);  t = RN32(w * decay);  r = RN32(t - eta*v);  split(r).
 
-    ``v`` holds bf16 values (float64 array), ``eta`` is a float32 scalar or an
-    array broadcastable to v (one value per slot), ``decay`` a float32 scalar.
+    ``v`` holds bf16 values (float64 array), ``eta`` and ``decay`` are float32
+    scalars or arrays broadcastable to v (one value per slot).
     The decay multiply comes before the update (Record 7 page, section 4.1).
     w*decay and eta*v are exact in float64 (<=48- and <=32-bit significands);
     t - eta*v is exact unless TwoSum reports an error, and those elements are
@@ -275,7 +280,7 @@ def mp_apply_update(w_hi, w_lo, v, eta, decay: float):
     w = recombine(w_hi, w_lo).view(np.float32).astype(np.float64)
     v = np.asarray(v, dtype=np.float64)
     eta_b = np.broadcast_to(np.asarray(eta, dtype=np.float64), v.shape)
-    t = round_to_f32(w * decay)
+    t = round_to_f32(w * np.asarray(decay, dtype=np.float64))
     prod = eta_b * v
     s = t - prod
     bb = s - t
@@ -294,7 +299,7 @@ def mp_apply_update(w_hi, w_lo, v, eta, decay: float):
 
 def muon_bank_step(grad, buf, w_hi, w_lo, storage: str, *, lr: float = 0.02,
                    weight_decay: float = 0.01, momentum: float = 0.95,
-                   lr_mul: float = 1.0, wd_mul: float = 1.0, lr_mul_per_slot=None,
+                   lr_mul: float = 1.0, wd_mul: float = 1.0, lr_mul_per_slot=None, slot_scalars=None,
                    steps: int = NS_STEPS, a: float = NS_COEFFS[0], b: float = NS_COEFFS[1],
                    c: float = NS_COEFFS[2], eps: float = NS_EPS, schedule=None) -> dict:
     """One Muon step on a viewed bank [batch, rows, cols].
@@ -304,18 +309,30 @@ def muon_bank_step(grad, buf, w_hi, w_lo, storage: str, *, lr: float = 0.02,
     defaults are Muon's constructor defaults lr=0.02, weight_decay=0.01,
     momentum=0.95 ("Muon Custom Sizing", section 2.2).  ``lr_mul_per_slot``
     (float32 values, one per slot) multiplies eta once more in float32.
-    Dead (all-zero) slots need no special case: every stage maps zero to zero."""
+    ``slot_scalars`` ([batch, 4] float32 values: mu, nu, decay, eta of each
+    slot) replaces all of these per slot: every bank's momentum, decay and
+    per-matrix learning rate held in one float32 table, as the "Unified
+    zero-copy optimizer and transposed LM head" page, section 4, keeps them in
+    one device buffer uploaded once per step.  Dead (all-zero) slots need no
+    special case: every stage maps zero to zero."""
     grad = np.asarray(grad, dtype=np.float64)
     _, rows, cols = grad.shape
     sc = step_scalars(lr, weight_decay, momentum, rows, cols, lr_mul, wd_mul)
-    buf_new, u = momentum_nesterov(grad, buf, sc.mu, sc.nu, storage)
+    if slot_scalars is not None:
+        if lr_mul_per_slot is not None:
+            raise ValueError("slot_scalars already holds each slot's eta")
+        tab = np.asarray(slot_scalars, dtype=np.float64).reshape(grad.shape[0], 4)
+        mu, nu, decay, eta = (tab[:, k][:, None, None] for k in range(4))
+    else:
+        mu, nu, decay = sc.mu, sc.nu, sc.decay
+        if lr_mul_per_slot is None:
+            eta = sc.eta
+        else:
+            per = np.asarray(lr_mul_per_slot, dtype=np.float64)
+            eta = round_to_f32(sc.eta * per)[:, None, None]
+    buf_new, u = momentum_nesterov(grad, buf, mu, nu, storage)
     v64 = newton_schulz(u, steps, a, b, c, eps, schedule=schedule)
     v = round_to_bf16(v64)
-    if lr_mul_per_slot is None:
-        eta = sc.eta
-    else:
-        per = np.asarray(lr_mul_per_slot, dtype=np.float64)
-        eta = round_to_f32(sc.eta * per)[:, None, None]
-    hi, lo = mp_apply_update(w_hi, w_lo, v, eta, sc.decay)
+    hi, lo = mp_apply_update(w_hi, w_lo, v, eta, decay)
     return {"momentum": buf_new, "u": u, "v64": v64, "v": v, "w_hi": hi, "w_lo": lo,
-            "scalars": sc, "eta": eta}
+            "scalars": sc, "eta": eta, "decay": decay}

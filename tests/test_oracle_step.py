@@ -97,3 +97,40 @@ def test_fp32_config_zero_momentum_closed_form():
     sc = out["scalars"]
     np.testing.assert_array_equal(out["momentum"], (sc.nu * g).astype(np.float32).astype(np.float64))
     assert CONFIGS[0][0].grad_dtype == "f32"
+
+
+def test_slot_scalar_table_is_applied_per_slot_exactly():
+    """With a per-slot table of (mu, nu, decay, eta), slot i's buf', u and weights are the exactly rounded
+    values of slot i's own scalars, checked element by element in exact rationals; the scalars are
+    arbitrary float32 values (nu need not be 1 - mu)."""
+    bank = make_random_bank(10, 3, 4, 5)
+    g = _vals(bank, "grad", "bf16")
+    m = _vals(bank, "momentum", "bf16")
+    tab = np.array([[0.9, 0.1, 0.999, 0.03], [0.95, 0.05, 0.9998, 0.02], [0.8, 0.3, 0.75, 0.011]],
+                   dtype=np.float32)
+    out = muon_bank_step(g, m, bank["w_hi"], bank["w_lo"], BF16, slot_scalars=tab)
+    w_old = recombine(bank["w_hi"], bank["w_lo"]).view(np.float32).astype(np.float64)
+    w_new = recombine(out["w_hi"], out["w_lo"]).view(np.float32).astype(np.float64)
+    for i in range(3):
+        mu, nu, d, eta = (Fraction(float(x)) for x in tab[i])
+        for j in np.ndindex(g.shape[1:]):
+            b_new = round_fraction(mu * Fraction(float(m[i][j])) + nu * Fraction(float(g[i][j])), 8, -126, 127)
+            assert out["momentum"][i][j] == b_new
+            u = round_fraction(nu * Fraction(float(g[i][j])) + mu * Fraction(b_new), 8, -126, 127)
+            assert out["u"][i][j] == u
+            t = round_fraction(Fraction(float(w_old[i][j])) * d, 24, -126, 127)
+            r = round_fraction(Fraction(t) - eta * Fraction(float(out["v"][i][j])), 24, -126, 127)
+            assert w_new[i][j] == r
+
+
+def test_slot_scalar_table_with_the_call_scalars_is_the_plain_step():
+    """A table that holds the call's own scalars in every slot gives the plain step's bits."""
+    bank = make_random_bank(11, 3, 6, 4)
+    g = _vals(bank, "grad", "bf16")
+    m = _vals(bank, "momentum", "bf16")
+    base = muon_bank_step(g, m, bank["w_hi"], bank["w_lo"], BF16)
+    sc = base["scalars"]
+    tab = np.tile(np.array([[sc.mu, sc.nu, sc.decay, sc.eta]], dtype=np.float32), (3, 1))
+    out = muon_bank_step(g, m, bank["w_hi"], bank["w_lo"], BF16, slot_scalars=tab)
+    for k in ("momentum", "u", "v", "w_hi", "w_lo"):
+        np.testing.assert_array_equal(out[k], base[k])
