@@ -76,6 +76,14 @@ typedef struct {
      * coefficients are named on the "Unified zero-copy optimizer" page
      * (sections 1.3, 4) without values, so the caller supplies them. */
     const double *ns_schedule;
+    /* Optional per-slot scalar table, the one device buffer of bank scalars that the "Unified zero-copy
+     * optimizer and transposed LM head" page (section 4) uploads once per step and graph replays read:
+     * NULL (the default) uses the scalars above and each bank's multipliers; otherwise a DEVICE array
+     * of 4 floats per slot, (mu, nu, decay, eta), for the slots of all banks of the call in bank order,
+     * 16-byte aligned.  The kernels read it when they run, so a captured step sees the values in the
+     * buffer at each replay.  The banks' lr_mul_per_slot must then be NULL (MB_ERR_VALUE).
+     * mb_slot_scalars_fill writes the table that reproduces the call's own scalars. */
+    const float *slot_scalars;
 } mb_hparams;
 
 /* One viewed bank [batch, rows, cols] (e.g. attention QKVO (10, 3072, 768)
@@ -101,6 +109,28 @@ const char *mb_status_string(int32_t status);
 const char *mb_last_error(void);
 /* Library version string. */
 const char *mb_version(void);
+
+/* Host helper for hp.slot_scalars: for each slot i of the banks in order, writes (mu, nu, decay, eta)
+ * into host_table[4i .. 4i+3], as muon_bank_step derives them from hp (NULL = defaults) and each bank's
+ * lr_mul and wd_mul: binary64 arithmetic rounded once to float32.  capacity is the number of floats at
+ * host_table (at least 4 per slot, else MB_ERR_WORKSPACE).  A bank with lr_mul_per_slot (a device
+ * vector the host cannot read) is MB_ERR_VALUE: fold the multiplier into the table's eta instead.  The
+ * caller edits the rows it wants (schedules, per-matrix rates) and uploads the table. */
+mb_status mb_slot_scalars_fill(const mb_bank *banks, int32_t num_banks, const mb_hparams *hp,
+                               float *host_table, int64_t capacity);
+
+/* What muon_bank_step would enqueue for these banks on a device with num_xcds XCDs (MI355X: 8), under
+ * the current mb_ns_set_path setting: kernel launches by kind (total excludes the device-to-device
+ * copies of one-round calls), and the tile edge of each persistent launch.  Every persistent launch's
+ * task lists are checked on the host with the kernel's own decode: each task of each slot listed
+ * exactly once, on its slot's queue, after every task it waits for (MB_ERR_VALUE with the reason if
+ * not).  Host only; touches no device. */
+typedef struct {
+    int32_t momentum, ns_scale, ns_persist, ns_small, ns_per_contraction, apply, copies, total;
+    int32_t persist_tile[8];
+} mb_step_plan_info;
+mb_status mb_step_plan(const mb_bank *banks, int32_t num_banks, const mb_hparams *hp, int32_t num_xcds,
+                       mb_step_plan_info *out);
 
 /* Workspace bytes needed by muon_bank_step for these banks (0 on invalid shapes). */
 size_t mb_step_workspace_bytes(const mb_bank *banks, int32_t num_banks);

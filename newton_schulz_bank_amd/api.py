@@ -40,7 +40,8 @@ class MuonBankError(RuntimeError):
 class mb_hparams(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_double), ("weight_decay", ctypes.c_double), ("momentum", ctypes.c_double),
                 ("ns_steps", ctypes.c_int32), ("a", ctypes.c_double), ("b", ctypes.c_double),
-                ("c", ctypes.c_double), ("eps", ctypes.c_double), ("ns_schedule", ctypes.c_void_p)]
+                ("c", ctypes.c_double), ("eps", ctypes.c_double), ("ns_schedule", ctypes.c_void_p),
+                ("slot_scalars", ctypes.c_void_p)]
 
 
 class mb_bank(ctypes.Structure):
@@ -51,13 +52,19 @@ class mb_bank(ctypes.Structure):
                 ("u_out", ctypes.c_void_p)]
 
 
+class mb_step_plan_info(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_int32) for k in ("momentum", "ns_scale", "ns_persist", "ns_small", "ns_per_contraction",
+                                              "apply", "copies", "total")] + [("persist_tile", ctypes.c_int32 * 8)]
+
+
 class mb_kernel_time(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
 
 
 _lib = None
 
-EXPORTED = ("mb_default_hparams", "mb_status_string", "mb_last_error", "mb_version", "mb_step_workspace_bytes",
+EXPORTED = ("mb_default_hparams", "mb_status_string", "mb_last_error", "mb_version", "mb_slot_scalars_fill",
+            "mb_step_plan", "mb_step_workspace_bytes",
             "mb_ns_workspace_bytes", "muon_bank_step", "muon_momentum_update", "ns_orthogonalize_batched",
             "ns_orthogonalize_batched_sched", "ns_orthogonalize_batched_noalloc", "mp_apply_update", "transpose_copy", "transpose_add", "mb_ns_set_path", "mb_device_fault", "mb_timing_enable", "mb_timing_read")
 
@@ -78,6 +85,9 @@ def lib() -> ctypes.CDLL:
         "mb_last_error": (ctypes.c_char_p, []),
         "mb_version": (ctypes.c_char_p, []),
         "mb_step_workspace_bytes": (sz, [ctypes.POINTER(mb_bank), i32]),
+        "mb_slot_scalars_fill": (i32, [ctypes.POINTER(mb_bank), i32, ctypes.POINTER(mb_hparams), vp, i64]),
+        "mb_step_plan": (i32, [ctypes.POINTER(mb_bank), i32, ctypes.POINTER(mb_hparams), i32,
+                               ctypes.POINTER(mb_step_plan_info)]),
         "mb_ns_workspace_bytes": (sz, [i64, i64, i64]),
         "muon_bank_step": (i32, [ctypes.POINTER(mb_bank), i32, ctypes.POINTER(mb_hparams), vp, sz, vp]),
         "muon_momentum_update": (i32, [vp, vp, vp, i64, i64, i64, i32, f32, f32, vp]),
@@ -159,7 +169,7 @@ def make_hparams(schedule=None, **kw) -> mb_hparams:
     schedule array alive."""
     hp = default_hparams()
     for k, v in kw.items():
-        if not hasattr(hp, k) or k == "ns_schedule":
+        if not hasattr(hp, k) or k in ("ns_schedule", "slot_scalars"):
             raise KeyError(k)
         setattr(hp, k, v)
     if schedule is not None:
@@ -211,6 +221,37 @@ class Bank:
                        _ptr(self.u_out))
 
 
+def slot_scalars_table(banks, hp: mb_hparams | None = None):
+    """numpy float32 [total slots, 4]: (mu, nu, decay, eta) of every slot of the banks in order, as the
+    step derives them (mb_slot_scalars_fill); edit rows, upload, and pass it with ``with_slot_scalars``."""
+    import numpy as np
+    cb = [b.to_c() for b in banks]
+    arr = (mb_bank * len(cb))(*cb)
+    n = sum(int(c.batch) for c in cb)
+    out = np.zeros((n, 4), dtype=np.float32)
+    _check(lib().mb_slot_scalars_fill(arr, len(cb), ctypes.byref(hp) if hp is not None else None,
+                                      out.ctypes.data, out.size))
+    return out
+
+
+def with_slot_scalars(hp: mb_hparams | None, table: torch.Tensor | None) -> mb_hparams:
+    """A copy of hp (defaults if None) whose per-slot scalar table is the device tensor ``table``
+    (float32 [total slots, 4], contiguous); None clears it.  The struct keeps the tensor alive."""
+    out = mb_hparams()
+    ctypes.pointer(out)[0] = hp if hp is not None else default_hparams()
+    if hp is not None and hasattr(hp, "_schedule_keepalive"):
+        out._schedule_keepalive = hp._schedule_keepalive
+    if table is None:
+        out.slot_scalars = None
+        return out
+    _dense(table, "slot_scalars", 4)
+    if table.dtype != torch.float32 or table.dim() != 2 or table.shape[1] != 4:
+        raise ValueError("slot_scalars must be float32 [total slots, 4]")
+    out.slot_scalars = table.data_ptr()
+    out._slot_scalars_keepalive = table
+    return out
+
+
 def mb_step_workspace_bytes(banks) -> int:
     arr = (mb_bank * len(banks))(*[b.to_c() for b in banks])
     return int(lib().mb_step_workspace_bytes(arr, len(banks)))
@@ -232,6 +273,9 @@ def muon_bank_step(banks, hp: mb_hparams | None = None, workspace: torch.Tensor 
     if isinstance(banks, Bank):
         banks = [banks]
     cbanks = [b.to_c() for b in banks]
+    table = getattr(hp, "_slot_scalars_keepalive", None) if hp is not None and hp.slot_scalars else None
+    if table is not None and table.shape[0] != sum(int(c.batch) for c in cbanks):
+        raise ValueError("slot_scalars must have one row per slot of the banks")
     arr = (mb_bank * len(cbanks))(*cbanks)
     need = int(lib().mb_step_workspace_bytes(arr, len(cbanks)))
     ws = _workspace(need, banks[0].grad, workspace)

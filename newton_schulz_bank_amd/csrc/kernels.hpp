@@ -14,26 +14,65 @@ struct RoundTimer {
     virtual ~RoundTimer() = default;
 };
 
-// Elements per workgroup chunk of the streaming kernels and the chunk count per slot.
-int64_t stream_chunk_elems(bool vec);
-int stream_chunks(int64_t slot_numel, bool vec);
+// Elements per workgroup of the streaming kernels (and per partial sum of u^2): two 8-element groups
+// per thread of 256, so that many short workgroups are in flight (16384 per workgroup measured 9 %
+// slower for momentum, 4 % for the apply).
+constexpr int64_t kStreamChunk = 4096;
+// Banks per launch of the streaming kernels (momentum, scale, apply); more take several launches.
+constexpr int kMaxStreamBanks = 16;
+int stream_chunks(int64_t slot_numel);
 
-// buf' and u (and, if partials is non-null, per-(slot, chunk) sums of u^2 in binary64).
-hipError_t launch_momentum(const void* grad, void* buf, uint16_t* u, double* partials, int64_t batch,
-                           int64_t slot_numel, bool f32, bool vec, float mu, float nu, hipStream_t stream);
+// buf' and u of one bank (and, if partials is non-null, per-(slot, chunk) sums of u^2 in binary64).
+// slot_base: the bank's first row in the call's per-slot scalar table.
+struct MomentumBank {
+    const void* grad;
+    void* buf;
+    uint16_t* u;
+    double* partials;
+    int64_t batch, slot_numel;
+    bool f32;
+    float mu, nu;
+    int slot_base;
+};
+// Momentum of several banks, one launch per kMaxStreamBanks.  slot_scalars: NULL, or a device table
+// of 4 floats (mu, nu, decay, eta) per slot of the call, whose mu and nu replace the banks' own.
+hipError_t launch_momentum(const MomentumBank* banks, int nbanks, const float* slot_scalars, hipStream_t stream);
+
+// The mixed-precision apply on one bank [batch, slot_numel]: eta per slot is eta, or
+// RN32(eta * lr_mul_per_slot[i]), or (with a scalar table) the table's eta; decay likewise.
+struct ApplyBank {
+    uint16_t* w_hi;
+    uint16_t* w_lo;
+    const uint16_t* v;
+    const float* lr_mul_per_slot;
+    int64_t batch, slot_numel;
+    float eta, decay;
+    int slot_base;
+};
+hipError_t launch_apply(const ApplyBank* banks, int nbanks, const float* slot_scalars, hipStream_t stream);
+
 // Per-(slot, chunk) sums of x^2 of a bf16 bank, in binary64.
-hipError_t launch_sumsq(const uint16_t* x, double* partials, int64_t batch, int64_t slot_numel, bool vec,
-                        hipStream_t stream);
-// Per slot i, from the sum S of its partials: live[i] = 0 if S == 0 (every element zero), else a live word
-// (common.hpp); scale[i] = 1 / (sqrt(S) + eps), or for a pre-scaled slot 2^-k / (sqrt(S) + eps) with
-// xpre's slot i = x0's slot i * 2^k.  Also clears, if non-null, heads[0, 32) (queue heads, error word and
-// exit count of a persistent launch) and ctr[i].
-hipError_t launch_ns_scale(const double* partials, int nchunks, int64_t batch, double eps, float* scale, int* live,
-                           int* heads, int* ctr, const uint16_t* x0, uint16_t* xpre, int64_t slot_numel,
-                           hipStream_t stream);
-// The mixed-precision apply on [batch, slot_numel].
-hipError_t launch_apply(uint16_t* w_hi, uint16_t* w_lo, const uint16_t* v, int64_t batch, int64_t slot_numel,
-                        bool vec, float eta, float decay, const float* lr_mul_per_slot, hipStream_t stream);
+hipError_t launch_sumsq(const uint16_t* x, double* partials, int64_t batch, int64_t slot_numel, hipStream_t stream);
+
+// Per slot i of one bank, from the sum S of its partials: live[i] = 0 if S == 0 (every element zero),
+// else a live word (common.hpp); scale[i] = 1 / (sqrt(S) + eps), or for a pre-scaled slot
+// 2^-k / (sqrt(S) + eps) with xpre's slot i = x0's slot i * 2^k.  Also clears, if non-null, heads[0, 32)
+// (queue heads, error word and exit count of a persistent launch) and ctr[i].  first_slot is set by
+// the launcher.
+struct ScaleBank {
+    const double* partials;
+    int nchunks;
+    int64_t batch;
+    float* scale;
+    int* live;
+    int* heads;
+    int* ctr;
+    const uint16_t* x0;
+    uint16_t* xpre;
+    int64_t slot_numel;
+    int first_slot;
+};
+hipError_t launch_ns_scale(const ScaleBank* banks, int nbanks, double eps, hipStream_t stream);
 
 // One Newton-Schulz round on a bank: x_out = round(x_in), with A and Bm as scratch.
 struct NsRound {
@@ -88,23 +127,26 @@ bool ns_persist_supported();
 bool ns_persist_fits256(int64_t rows, int64_t cols);
 hipError_t ns_persist(const NsPersistBank* banks, int nbanks, int tile, const NsCoef* coef, int steps, int* sync,
                       hipStream_t stream);
+// Host check of one persistent launch's task lists with nq queues, by the kernel's own decode: every
+// task of every slot's chains listed exactly once, on its slot's queue, each after every task it waits
+// for.  On failure returns false with a reason in why.
+bool ns_persist_check(const NsPersistBank* banks, int nbanks, int tile, int steps, int nq, char* why, size_t why_len);
 // The current device's persistent-launch fault flag (1: a dependency wait hit its time cap since the
 // flag was last cleared); blocking; clears it when `clear` is set.
 hipError_t ns_persist_fault(int* flag, bool clear);
 
-// Every Newton-Schulz round of a bank of small slots (Gram side <= 64, <= 4096 elements) in one
-// launch, one workgroup per slot (x0 -> dest; dest may equal x0).
+// Every Newton-Schulz round of banks of small slots (Gram side <= 64, <= 4096 elements) in one launch
+// per kMaxSmallBanks banks, one workgroup per slot (x0 -> dest; dest may equal x0).
+constexpr int kMaxSmallBanks = 8;
 struct NsSmall {
     const uint16_t* x0;
     uint16_t* dest;
     const float* scale;
     const int* live;
     int64_t batch, rows, cols;
-    int steps;
-    const NsCoef* coef;
 };
 bool ns_small_eligible(int64_t rows, int64_t cols, int steps);
-hipError_t ns_small(const NsSmall& r, hipStream_t stream);
+hipError_t ns_small(const NsSmall* banks, int nbanks, int steps, const NsCoef* coef, hipStream_t stream);
 
 // dst [cols, rows] = src^T (add: dst += src^T, one rounding), elements of 2 or 4 bytes.
 hipError_t launch_transpose(void* dst, const void* src, int64_t rows, int64_t cols, int elem_bytes, bool add,

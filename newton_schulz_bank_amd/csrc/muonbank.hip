@@ -167,7 +167,7 @@ BankWs bank_ws_layout(int64_t batch, int64_t rows, int64_t cols, bool vec) {
     w.x2 = off; off += xb;
     w.A = off; off += ab;
     w.Bm = off; off += ab;
-    w.partials = off; off += round_up((size_t)batch * mb::stream_chunks(rows * cols, vec) * 8);
+    w.partials = off; off += round_up((size_t)batch * mb::stream_chunks(rows * cols) * 8);
     w.scale = off; off += round_up((size_t)batch * 4);
     w.live = off; off += round_up((size_t)batch * 4);
     w.sync = off; off += round_up((size_t)(32 + batch) * 4);
@@ -229,6 +229,17 @@ StepPlan plan_step(const mb_bank* banks, int32_t num_banks) {
 // contraction.
 std::atomic<int> g_ns_path{0};
 
+// The float32 scalars of one bank, each from double arithmetic rounded once ("Muon Custom Sizing",
+// section 4: eff_lr = lr * max(1, rows/cols)^0.5 * lr_mul, eff_wd = lr * wd * wd_mul, and the
+// momentum's two lerp weights).
+struct BankScalars {
+    float mu, nu, decay, eta;
+};
+BankScalars bank_scalars(const mb_bank& b, const mb_hparams& hp) {
+    return {f32(hp.momentum), f32(1.0 - hp.momentum), f32(1.0 - hp.lr * hp.weight_decay * b.wd_mul),
+            f32(hp.lr * std::sqrt(std::max(1.0, (double)b.rows / (double)b.cols)) * b.lr_mul)};
+}
+
 // Newton-Schulz rounds on scaled input: x_first -> ... -> dest.  x1, x2 are ping-pong buffers
 // distinct from x_first and dest; sync (cleared by the ns_scale launch) serves the persistent
 // kernel.
@@ -260,9 +271,9 @@ mb_status run_ns(const uint16_t* x_first, uint16_t* dest, uint16_t* x1, uint16_t
         return MB_OK;
     }
     if (g_ns_path.load() == 0 && mb::ns_small_eligible(rows, cols, steps)) {
-        mb::NsSmall r{x_first, dest, scale, live, batch, rows, cols, steps, coef.data()};
+        const mb::NsSmall r{x_first, dest, scale, live, batch, rows, cols};
         timer.begin("ns_small", stream);
-        hipError_t e = mb::ns_small(r, stream);
+        hipError_t e = mb::ns_small(&r, 1, steps, coef.data(), stream);
         timer.end(stream);
         if (e != hipSuccess) return fail(MB_ERR_HIP, "Newton-Schulz launch: %s", hipGetErrorString(e));
         return MB_OK;
@@ -296,6 +307,7 @@ void mb_default_hparams(mb_hparams* hp) {
     hp->c = 2.0315;
     hp->eps = 1e-7;
     hp->ns_schedule = nullptr;
+    hp->slot_scalars = nullptr;
 }
 
 const char* mb_status_string(int32_t s) {
@@ -321,6 +333,88 @@ size_t mb_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols) {
     if (check_shape(batch, rows, cols, "mb_ns_workspace_bytes") != MB_OK) return 0;
     const bool vec = (rows * cols) % 8 == 0;
     return bank_ws_layout(batch, rows, cols, vec).total;
+}
+
+mb_status mb_slot_scalars_fill(const mb_bank* banks, int32_t num_banks, const mb_hparams* hp_in, float* host_table,
+                               int64_t capacity) {
+    if (!banks || !host_table) return fail(MB_ERR_NULL, "mb_slot_scalars_fill: null pointer");
+    if (num_banks <= 0 || num_banks > 1024) return fail(MB_ERR_SHAPE, "mb_slot_scalars_fill: num_banks must be in 1..1024");
+    mb_hparams hp;
+    if (hp_in) hp = *hp_in;
+    else mb_default_hparams(&hp);
+    mb_status s = check_hparams(hp);
+    if (s != MB_OK) return s;
+    int64_t slots = 0;
+    for (int32_t i = 0; i < num_banks; ++i) {
+        const mb_bank& b = banks[i];
+        s = check_shape(b.batch, b.rows, b.cols, "mb_slot_scalars_fill");
+        if (s != MB_OK) return s;
+        if (!is_finite(b.lr_mul) || !is_finite(b.wd_mul)) return fail(MB_ERR_VALUE, "mb_slot_scalars_fill: bank %d multipliers", i);
+        if (b.lr_mul_per_slot)
+            return fail(MB_ERR_VALUE, "mb_slot_scalars_fill: bank %d has lr_mul_per_slot (a device vector): fold it "
+                        "into the table's eta", i);
+        slots += b.batch;
+    }
+    if (capacity < 4 * slots)
+        return fail(MB_ERR_WORKSPACE, "mb_slot_scalars_fill: %lld floats needed, %lld given", (long long)(4 * slots),
+                    (long long)capacity);
+    float* out = host_table;
+    for (int32_t i = 0; i < num_banks; ++i) {
+        const BankScalars bs = bank_scalars(banks[i], hp);
+        for (int64_t k = 0; k < banks[i].batch; ++k, out += 4) {
+            out[0] = bs.mu;
+            out[1] = bs.nu;
+            out[2] = bs.decay;
+            out[3] = bs.eta;
+        }
+    }
+    return ok();
+}
+
+mb_status mb_step_plan(const mb_bank* banks, int32_t num_banks, const mb_hparams* hp_in, int32_t num_xcds,
+                       mb_step_plan_info* out) {
+    if (!banks || !out) return fail(MB_ERR_NULL, "mb_step_plan: null pointer");
+    if (num_banks <= 0 || num_banks > 1024) return fail(MB_ERR_SHAPE, "mb_step_plan: num_banks must be in 1..1024");
+    mb_hparams hp;
+    if (hp_in) hp = *hp_in;
+    else mb_default_hparams(&hp);
+    mb_status s = check_hparams(hp);
+    if (s != MB_OK) return s;
+    for (int32_t i = 0; i < num_banks; ++i) {
+        s = check_shape(banks[i].batch, banks[i].rows, banks[i].cols, "mb_step_plan");
+        if (s != MB_OK) return s;
+    }
+    mb_step_plan_info info{};
+    const int groups = (num_banks + mb::kMaxStreamBanks - 1) / mb::kMaxStreamBanks;
+    info.momentum = info.ns_scale = info.apply = groups;
+    const bool persist = g_ns_path.load() == 0 && num_xcds >= 1 && num_xcds <= 16;
+    const StepPlan plan = plan_step(banks, num_banks);
+    int small = 0;
+    for (int32_t i = 0; i < num_banks; ++i) {
+        const mb_bank& b = banks[i];
+        if (hp.ns_steps == 1 && !b.v_out) ++info.copies;
+        if (persist && plan.chunk_of[(size_t)i] >= 0) continue;
+        if (g_ns_path.load() == 0 && mb::ns_small_eligible(b.rows, b.cols, hp.ns_steps)) ++small;
+        else info.ns_per_contraction += 3 * hp.ns_steps;
+    }
+    info.ns_small = (small + mb::kMaxSmallBanks - 1) / mb::kMaxSmallBanks;
+    if (persist) {
+        char why[256];
+        for (const PersistChunk& c : plan.chunks) {
+            std::vector<mb::NsPersistBank> pb;
+            for (int32_t i : c.banks)
+                pb.push_back({nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, banks[i].batch,
+                              banks[i].rows, banks[i].cols});
+            if (!mb::ns_persist_check(pb.data(), (int)pb.size(), c.tile, hp.ns_steps, num_xcds, why, sizeof why))
+                return fail(MB_ERR_VALUE, "mb_step_plan: persistent launch of %zu banks, %d-tiles: %s", c.banks.size(),
+                            c.tile, why);
+            ++info.ns_persist;
+            info.persist_tile[info.ns_persist - 1 < 8 ? info.ns_persist - 1 : 7] = c.tile;
+        }
+    }
+    info.total = info.momentum + info.ns_scale + info.ns_persist + info.ns_small + info.ns_per_contraction + info.apply;
+    *out = info;
+    return ok();
 }
 
 size_t mb_step_workspace_bytes(const mb_bank* banks, int32_t num_banks) {
@@ -350,11 +444,10 @@ mb_status muon_momentum_update(const void* grad, void* momentum, uint16_t* u_out
                           {(uintptr_t)momentum, (uintptr_t)momentum + n * es, "momentum"},
                           {(uintptr_t)u_out, (uintptr_t)u_out + n * 2, "u_out"}});
     if (s != MB_OK) return s;
-    const bool vec = (rows * cols) % 8 == 0;
     Timer timer;
     timer.begin("momentum", (hipStream_t)stream);
-    hipError_t e = mb::launch_momentum(grad, momentum, u_out, nullptr, batch, rows * cols, dtype == MB_F32, vec, mu, nu,
-                                       (hipStream_t)stream);
+    const mb::MomentumBank mbk{grad, momentum, u_out, nullptr, batch, rows * cols, dtype == MB_F32, mu, nu, 0};
+    hipError_t e = mb::launch_momentum(&mbk, 1, nullptr, (hipStream_t)stream);
     timer.end((hipStream_t)stream);
     if (e != hipSuccess) return fail(MB_ERR_HIP, "momentum launch: %s", hipGetErrorString(e));
     return ok();
@@ -402,13 +495,14 @@ mb_status ns_orthogonalize_impl(const uint16_t* x, uint16_t* y, int64_t batch, i
     uint16_t* x2 = (uint16_t*)(ws + L.x2);
     Timer timer;
     timer.begin("sumsq", st);
-    hipError_t e = mb::launch_sumsq(x, partials, batch, rows * cols, vec, st);
+    hipError_t e = mb::launch_sumsq(x, partials, batch, rows * cols, st);
     timer.end(st);
     if (e != hipSuccess) return fail(MB_ERR_HIP, "sumsq launch: %s", hipGetErrorString(e));
     timer.begin("ns_scale", st);
     int* sync = (int*)(ws + L.sync);
-    e = mb::launch_ns_scale(partials, mb::stream_chunks(rows * cols, vec), batch, eps, scale, live, sync, sync + 32, x,
-                            mb::ns_prescale_buffer(x1, x2, steps), rows * cols, st);
+    const mb::ScaleBank sb{partials, mb::stream_chunks(rows * cols), batch, scale, live, sync, sync + 32, x,
+                           mb::ns_prescale_buffer(x1, x2, steps), rows * cols, 0};
+    e = mb::launch_ns_scale(&sb, 1, eps, st);
     timer.end(st);
     if (e != hipSuccess) return fail(MB_ERR_HIP, "ns_scale launch: %s", hipGetErrorString(e));
     // in place with a single round: write the round to scratch, then copy
@@ -513,8 +607,8 @@ mb_status mp_apply_update(uint16_t* w_hi, uint16_t* w_lo, const uint16_t* v, int
     if (s != MB_OK) return s;
     Timer timer;
     timer.begin("apply", (hipStream_t)stream);
-    hipError_t e = mb::launch_apply(w_hi, w_lo, v, batch, slot_numel, slot_numel % 8 == 0, eff_lr, decay,
-                                    lr_mul_per_slot, (hipStream_t)stream);
+    const mb::ApplyBank ab{w_hi, w_lo, v, lr_mul_per_slot, batch, slot_numel, eff_lr, decay, 0};
+    hipError_t e = mb::launch_apply(&ab, 1, nullptr, (hipStream_t)stream);
     timer.end((hipStream_t)stream);
     if (e != hipSuccess) return fail(MB_ERR_HIP, "apply launch: %s", hipGetErrorString(e));
     return ok();
@@ -533,6 +627,7 @@ mb_status muon_bank_step(const mb_bank* banks, int32_t num_banks, const mb_hpara
     // ---- validate every bank before enqueueing anything
     std::vector<Range> ranges;
     size_t need = 0;
+    int64_t total_slots = 0;
     for (int32_t i = 0; i < num_banks; ++i) {
         const mb_bank& b = banks[i];
         if (!b.grad || !b.momentum || !b.w_hi || !b.w_lo)
@@ -556,6 +651,17 @@ mb_status muon_bank_step(const mb_bank* banks, int32_t num_banks, const mb_hpara
         if (b.lr_mul_per_slot)
             ranges.push_back({(uintptr_t)b.lr_mul_per_slot, (uintptr_t)b.lr_mul_per_slot + b.batch * 4, "lr_mul_per_slot"});
         need += bank_ws_layout(b.batch, b.rows, b.cols, (b.rows * b.cols) % 8 == 0).total;
+        total_slots += b.batch;
+    }
+    if (hp.slot_scalars) {
+        if ((uintptr_t)hp.slot_scalars & 15u)
+            return fail(MB_ERR_ALIGN, "muon_bank_step: slot_scalars must be 16-byte aligned");
+        for (int32_t i = 0; i < num_banks; ++i)
+            if (banks[i].lr_mul_per_slot)
+                return fail(MB_ERR_VALUE, "muon_bank_step: bank %d has lr_mul_per_slot, but slot_scalars already "
+                            "holds every slot's eta", i);
+        ranges.push_back({(uintptr_t)hp.slot_scalars, (uintptr_t)hp.slot_scalars + (size_t)total_slots * 16,
+                          "slot_scalars"});
     }
     const StepPlan plan = plan_step(banks, num_banks);
     const size_t banks_bytes = need;
@@ -593,7 +699,7 @@ mb_status muon_bank_step(const mb_bank* banks, int32_t num_banks, const mb_hpara
         Run& r = runs[(size_t)i];
         r.slot = b.rows * b.cols;
         r.vec = r.slot % 8 == 0;
-        r.nch = mb::stream_chunks(r.slot, r.vec);
+        r.nch = mb::stream_chunks(r.slot);
         const BankWs L = bank_ws_layout(b.batch, b.rows, b.cols, r.vec);
         char* bw = ws + off;
         off += L.total;
@@ -609,18 +715,19 @@ mb_status muon_bank_step(const mb_bank* banks, int32_t num_banks, const mb_hpara
         // with one round and no v_out, the round would read u while writing v in the same buffer
         r.dest = (hp.ns_steps == 1 && r.v == r.u) ? r.x2 : r.v;
     }
+    // momentum of every bank in one launch (per kMaxStreamBanks banks), then the scale
     const float mu = f32(hp.momentum);
     const float nu = f32(1.0 - hp.momentum);
+    std::vector<mb::MomentumBank> mbk;
+    std::vector<mb::ScaleBank> sbk;
+    int slot_base = 0;
     for (int32_t i = 0; i < num_banks; ++i) {
         const mb_bank& b = banks[i];
         const Run& r = runs[(size_t)i];
-        timer.begin("momentum", st);
-        hipError_t e = mb::launch_momentum(b.grad, b.momentum, r.u, r.partials, b.batch, r.slot,
-                                           b.grad_dtype == MB_F32, r.vec, mu, nu, st);
-        timer.end(st);
-        if (e != hipSuccess) return fail(MB_ERR_HIP, "momentum launch: %s", hipGetErrorString(e));
+        mbk.push_back({b.grad, b.momentum, r.u, r.partials, b.batch, r.slot, b.grad_dtype == MB_F32, mu, nu, slot_base});
+        slot_base += (int)b.batch;
         // a bank in a persistent launch clears its slot counters; the chunk's first bank clears
-        // the chunk's queue heads and error word
+        // the chunk's queue heads, error word and exit count
         int *heads = nullptr, *ctr = nullptr;
         const int ch = plan.chunk_of[(size_t)i];
         if (persist && ch >= 0) {
@@ -631,12 +738,17 @@ mb_status muon_bank_step(const mb_bank* banks, int32_t num_banks, const mb_hpara
             if (k == 0) heads = cs;
             ctr = cs + 32 + c.base[k];
         }
-        timer.begin("ns_scale", st);
-        e = mb::launch_ns_scale(r.partials, r.nch, b.batch, hp.eps, r.scale, r.live, heads, ctr, r.u,
-                                mb::ns_prescale_buffer(r.x1, r.x2, hp.ns_steps), r.slot, st);
-        timer.end(st);
-        if (e != hipSuccess) return fail(MB_ERR_HIP, "ns_scale launch: %s", hipGetErrorString(e));
+        sbk.push_back({r.partials, r.nch, b.batch, r.scale, r.live, heads, ctr, r.u,
+                       mb::ns_prescale_buffer(r.x1, r.x2, hp.ns_steps), r.slot, 0});
     }
+    timer.begin("momentum", st);
+    hipError_t e = mb::launch_momentum(mbk.data(), num_banks, hp.slot_scalars, st);
+    timer.end(st);
+    if (e != hipSuccess) return fail(MB_ERR_HIP, "momentum launch: %s", hipGetErrorString(e));
+    timer.begin("ns_scale", st);
+    e = mb::launch_ns_scale(sbk.data(), num_banks, hp.eps, st);
+    timer.end(st);
+    if (e != hipSuccess) return fail(MB_ERR_HIP, "ns_scale launch: %s", hipGetErrorString(e));
     if (persist) {
         for (const PersistChunk& c : plan.chunks) {
             std::vector<mb::NsPersistBank> pb;
@@ -652,26 +764,45 @@ mb_status muon_bank_step(const mb_bank* banks, int32_t num_banks, const mb_hpara
             if (e != hipSuccess) return fail(MB_ERR_HIP, "Newton-Schulz launch: %s", hipGetErrorString(e));
         }
     }
+    // banks of small slots: every round of all of them in one launch; the rest one launch per contraction
+    std::vector<mb::NsSmall> small;
     for (int32_t i = 0; i < num_banks; ++i) {
         if (persist && plan.chunk_of[(size_t)i] >= 0) continue;
         const mb_bank& b = banks[i];
         const Run& r = runs[(size_t)i];
+        if (g_ns_path.load() == 0 && mb::ns_small_eligible(b.rows, b.cols, hp.ns_steps)) {
+            small.push_back({r.u, r.dest, r.scale, r.live, b.batch, b.rows, b.cols});
+            continue;
+        }
         s = run_ns(r.u, r.dest, r.x1, r.x2, r.A, r.Bm, b.batch, b.rows, b.cols, coef, r.scale, r.live, nullptr, st,
                    timer);
         if (s != MB_OK) return s;
     }
+    if (!small.empty()) {
+        timer.begin("ns_small", st);
+        e = mb::ns_small(small.data(), (int)small.size(), hp.ns_steps, coef.data(), st);
+        timer.end(st);
+        if (e != hipSuccess) return fail(MB_ERR_HIP, "Newton-Schulz launch: %s", hipGetErrorString(e));
+    }
+    // every apply in one launch (per kMaxStreamBanks banks); host scalars in double, rounded once to
+    // float32
+    std::vector<mb::ApplyBank> abk;
+    slot_base = 0;
     for (int32_t i = 0; i < num_banks; ++i) {
         const mb_bank& b = banks[i];
         const Run& r = runs[(size_t)i];
-        // host scalars in double, rounded once to float32
-        const float decay = f32(1.0 - hp.lr * hp.weight_decay * b.wd_mul);
-        const float eta = f32(hp.lr * std::sqrt(std::max(1.0, (double)b.rows / (double)b.cols)) * b.lr_mul);
-        timer.begin("apply", st);
-        hipError_t e = mb::launch_apply(b.w_hi, b.w_lo, r.dest, b.batch, r.slot, r.vec, eta, decay, b.lr_mul_per_slot, st);
-        timer.end(st);
-        if (e != hipSuccess) return fail(MB_ERR_HIP, "apply launch: %s", hipGetErrorString(e));
+        const BankScalars bs = bank_scalars(b, hp);
+        abk.push_back({b.w_hi, b.w_lo, r.dest, b.lr_mul_per_slot, b.batch, r.slot, bs.eta, bs.decay, slot_base});
+        slot_base += (int)b.batch;
+    }
+    timer.begin("apply", st);
+    e = mb::launch_apply(abk.data(), num_banks, hp.slot_scalars, st);
+    timer.end(st);
+    if (e != hipSuccess) return fail(MB_ERR_HIP, "apply launch: %s", hipGetErrorString(e));
+    for (int32_t i = 0; i < num_banks; ++i) {
+        const Run& r = runs[(size_t)i];
         if (r.dest != r.v) {
-            e = hipMemcpyAsync(r.v, r.dest, (size_t)(b.batch * r.slot) * 2, hipMemcpyDeviceToDevice, st);
+            e = hipMemcpyAsync(r.v, r.dest, (size_t)(banks[i].batch * r.slot) * 2, hipMemcpyDeviceToDevice, st);
             if (e != hipSuccess) return fail(MB_ERR_HIP, "copy: %s", hipGetErrorString(e));
         }
     }

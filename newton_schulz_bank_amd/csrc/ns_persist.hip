@@ -31,8 +31,12 @@
 // gives up instead of spinning forever.  The last workgroup to leave checks that
 // every queue was drained (a queue that no workgroup served would leave its
 // tasks undone) and sets the error word otherwise.
+#include <cstdio>
+#include <vector>
+
 #include "common.hpp"
 #include "kernels.hpp"
+#include "ns_persist_plan.hpp"
 #include "ns_tile.hpp"
 
 namespace mb {
@@ -45,46 +49,10 @@ namespace {
 
 constexpr uint64_t kWaitCapTicks = 20000000;   // 200 ms of the 100 MHz constant clock
 constexpr int kXccIdReg = 20 | (0 << 6) | (15 << 11);   // hwreg(HW_REG_XCC_ID, 0, 16)
-constexpr int kMaxQueues = 16;
-
-struct PersistBank {
-    const uint16_t* x0;     // round input of round 0 (unscaled)
-    const uint16_t* xpre;   // round input of round 0 for pre-scaled slots (their live word says which)
-    uint16_t* xa;           // outputs of rounds 0, 2, 4, ... (except the last)
-    uint16_t* xb;           // outputs of rounds 1, 3, 5, ...
-    uint16_t* dest;         // output of the last round
-    uint16_t* A;
-    uint16_t* Bm;
-    const float* scale;
-    const int* live;
-    int64_t slot;           // elements per slot of X
-    int64_t mm;             // elements per slot of A, B
-    int m, n;               // Gram size and long side (m <= n)
-    int tm, tn;             // tiles along m and along n
-    int batch;
-    int base;               // number of the bank's first slot in the launch's slot sequence
-    int tall;
-};
-
-struct PersistArgs {
-    PersistBank bank[kMaxPersistBanks];
-    int nbanks, steps, nq;
-    int* heads;             // [nq] next task of each queue
-    int* err;               // set when a dependency wait hits its time cap or a queue is left undrained
-    int* exits;             // workgroups that have left the task loop
-    int* ctr;               // [total slots] tasks finished per slot
-    // per queue: tasks of one round, of its Gram block and of its polynomial block, and the
-    // number of slots of each bank on the queue
-    int per_round[kMaxQueues], blk_g[kMaxQueues], blk_p[kMaxQueues];
-    int ls[kMaxQueues][kMaxPersistBanks];
-    float coef[kMaxRounds][3];   // (a, b, c) of each round
-};
 
 __device__ __forceinline__ int ld_relaxed(const int* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-__host__ __device__ __forceinline__ int sym_count(int tm) { return tm * (tm + 1) / 2; }
 
 template <class C>
 __global__ void __launch_bounds__(C::NT, 2) ns_persist_kernel(PersistArgs p) {
@@ -111,29 +79,15 @@ __global__ void __launch_bounds__(C::NT, 2) ns_persist_kernel(PersistArgs p) {
     __syncthreads();
     int idx = __builtin_amdgcn_readfirstlane(s_task);
     while (idx >= 0 && idx < total) {
-        // ---- decode: round t, contraction (phase), bank, slot, tile
-        const int t = idx / per_round;
-        int r = idx - t * per_round;
-        int phase;
-        if (r < p.blk_g[q]) phase = 0;
-        else if ((r -= p.blk_g[q]) < p.blk_p[q]) phase = 1;
-        else { r -= p.blk_p[q]; phase = 2; }
-        int b = 0, ntile = 1;
-        for (; b < p.nbanks - 1; ++b) {
-            ntile = phase == 2 ? p.bank[b].tm * p.bank[b].tn : sym_count(p.bank[b].tm);
-            const int cnt = p.ls[q][b] * ntile;
-            if (r < cnt) break;
-            r -= cnt;
-        }
-        const PersistBank& bk = p.bank[b];
-        ntile = phase == 2 ? bk.tm * bk.tn : sym_count(bk.tm);
-        const int l = r / ntile, tile = r - l * ntile;
-        const int first = ((q - bk.base) % p.nq + p.nq) % p.nq;      // the bank's first slot on this queue
-        const int slot = first + l * p.nq;
+        // ---- decode: round t, contraction (phase), bank, slot, tile, and the slot's finished-task
+        // count this task waits for
+        // (every field is wave-uniform: readfirstlane keeps them in scalar registers)
+        const PersistTask task = decode_task(p, q, idx);
+        const int t = __builtin_amdgcn_readfirstlane(task.t), phase = __builtin_amdgcn_readfirstlane(task.phase);
+        const int slot = __builtin_amdgcn_readfirstlane(task.slot), tile = __builtin_amdgcn_readfirstlane(task.tile);
+        const int need = __builtin_amdgcn_readfirstlane(task.need);
+        const PersistBank& bk = p.bank[__builtin_amdgcn_readfirstlane(task.b)];
         int* ctr = p.ctr + bk.base + slot;
-        const int nG = sym_count(bk.tm);
-        const int chain = 2 * nG + bk.tm * bk.tn;                      // tasks per slot and round
-        const int need = t * chain + (phase == 0 ? 0 : phase == 1 ? nG : 2 * nG);
 
         if (leader && need > 0 && __builtin_amdgcn_readfirstlane(ld_relaxed(ctr)) < need) {
             const uint64_t t0 = wall_clock64();
@@ -305,6 +259,56 @@ hipError_t ns_persist_fault(int* flag, bool clear) {
     return hipMemcpyToSymbol(HIP_SYMBOL(g_persist_fault), &zero, sizeof(int), 0, hipMemcpyHostToDevice);
 }
 
+bool ns_persist_check(const NsPersistBank* banks, int nbanks, int tile, int steps, int nq, char* why, size_t why_len) {
+    auto bad = [&](const char* fmt, int a, int b2, int c) {
+        if (why && why_len) snprintf(why, why_len, fmt, a, b2, c);
+        return false;
+    };
+    if (nbanks < 1 || nbanks > kMaxPersistBanks || (tile != 256 && tile != 128) || steps < 1 || steps > kMaxRounds ||
+        nq < 1 || nq > kMaxQueues)
+        return bad("launch arguments out of range (banks %d, tile %d, queues %d)", nbanks, tile, nq);
+    PersistArgs p;
+    fill_persist_args(p, banks, nbanks, tile, nullptr, steps, nq, nullptr);
+    // seen[b][(slot * steps + t) * chain + position in the round's chain]
+    std::vector<std::vector<unsigned char>> seen((size_t)nbanks);
+    std::vector<std::vector<int>> count((size_t)nbanks);
+    for (int b = 0; b < nbanks; ++b) {
+        const PersistBank& k = p.bank[b];
+        if (k.tm < 1 || k.tn < 1 || k.m % tile || k.n % tile) return bad("bank %d: sides not multiples of the tile %d%c", b, tile, ' ');
+        const int chain = 2 * sym_count(k.tm) + k.tm * k.tn;
+        seen[(size_t)b].assign((size_t)k.batch * steps * chain, 0);
+        count[(size_t)b].assign((size_t)k.batch, 0);
+    }
+    for (int q = 0; q < nq; ++q) {
+        const int total = steps * p.per_round[q];
+        for (int idx = 0; idx < total; ++idx) {
+            const PersistTask k = decode_task(p, q, idx);
+            if (k.b < 0 || k.b >= nbanks) return bad("queue %d position %d: bank %d out of range", q, idx, k.b);
+            const PersistBank& bk = p.bank[k.b];
+            if (k.slot < 0 || k.slot >= bk.batch) return bad("queue %d position %d: slot %d out of range", q, idx, k.slot);
+            if ((bk.base + k.slot) % nq != q) return bad("queue %d position %d: slot %d belongs to another queue", q, idx, k.slot);
+            const int nG = sym_count(bk.tm), chain = 2 * nG + bk.tm * bk.tn;
+            const int ntile = k.phase == 2 ? bk.tm * bk.tn : nG;
+            if (k.t < 0 || k.t >= steps || k.phase < 0 || k.phase > 2 || k.tile < 0 || k.tile >= ntile)
+                return bad("queue %d position %d: round, contraction or tile %d out of range", q, idx, k.tile);
+            const int pos = k.t * chain + (k.phase == 0 ? 0 : k.phase == 1 ? nG : 2 * nG) + k.tile;
+            unsigned char& mark = seen[(size_t)k.b][(size_t)k.slot * steps * chain + pos];
+            if (mark) return bad("queue %d position %d: a task of slot %d listed twice", q, idx, k.slot);
+            mark = 1;
+            // the slot's tasks come in chain order, so everything this task waits for (need tasks) was
+            // listed, and therefore claimed, before it on the same queue
+            int& c = count[(size_t)k.b][(size_t)k.slot];
+            if (pos != c || k.need > pos || k.need != pos - k.tile)
+                return bad("queue %d position %d: slot %d out of chain order", q, idx, k.slot);
+            ++c;
+        }
+    }
+    for (int b = 0; b < nbanks; ++b)
+        for (size_t i = 0; i < seen[(size_t)b].size(); ++i)
+            if (!seen[(size_t)b][i]) return bad("bank %d: task %d of the chains never listed%c", b, (int)i, ' ');
+    return true;
+}
+
 bool ns_persist_supported() {
     DeviceShape d;
     return device_shape(&d) == hipSuccess && d.understood;
@@ -338,57 +342,7 @@ hipError_t ns_persist(const NsPersistBank* banks, int nbanks, int tile, const Ns
     if (e != hipSuccess) return e;
     if (!d.understood) return hipErrorNotSupported;
     PersistArgs p{};
-    p.nbanks = nbanks;
-    p.steps = steps;
-    p.nq = d.xccs;
-    p.heads = sync;
-    p.err = sync + 16;
-    p.exits = sync + 17;
-    p.ctr = sync + 32;
-    int base = 0;
-    for (int b = 0; b < nbanks; ++b) {
-        const NsPersistBank& r = banks[b];
-        PersistBank& k = p.bank[b];
-        k.tall = r.rows > r.cols ? 1 : 0;
-        k.x0 = r.x0;
-        k.xpre = ns_prescale_buffer(r.xa, r.xb, steps);
-        k.xa = r.xa;
-        k.xb = r.xb;
-        k.dest = r.dest;
-        k.A = r.A;
-        k.Bm = r.Bm;
-        k.scale = r.scale;
-        k.live = r.live;
-        k.slot = r.rows * r.cols;
-        k.m = (int)(k.tall ? r.cols : r.rows);
-        k.n = (int)(k.tall ? r.rows : r.cols);
-        k.mm = (int64_t)k.m * k.m;
-        k.tm = k.m / tile;
-        k.tn = k.n / tile;
-        k.batch = (int)r.batch;
-        k.base = base;
-        base += k.batch;
-    }
-    for (int q = 0; q < p.nq; ++q) {
-        int g = 0, pp = 0, u = 0;
-        for (int b = 0; b < nbanks; ++b) {
-            const PersistBank& k = p.bank[b];
-            const int first = ((q - k.base) % p.nq + p.nq) % p.nq;
-            const int ls = first < k.batch ? (k.batch - first + p.nq - 1) / p.nq : 0;
-            p.ls[q][b] = ls;
-            g += ls * sym_count(k.tm);
-            pp += ls * sym_count(k.tm);
-            u += ls * k.tm * k.tn;
-        }
-        p.blk_g[q] = g;
-        p.blk_p[q] = pp;
-        p.per_round[q] = g + pp + u;
-    }
-    for (int t = 0; t < steps; ++t) {
-        p.coef[t][0] = coef[t].a;
-        p.coef[t][1] = coef[t].b;
-        p.coef[t][2] = coef[t].c;
-    }
+    fill_persist_args(p, banks, nbanks, tile, coef, steps, d.xccs, sync);
     if (tile == 256) {
         // one 16-wavefront workgroup per CU (its 128 KiB ring fills the LDS)
         ns_persist_kernel<Cfg256><<<dim3((unsigned)d.cus), Cfg256::NT, 0, stream>>>(p);

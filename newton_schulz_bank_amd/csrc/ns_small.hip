@@ -24,27 +24,37 @@ constexpr int kSmallThreads = 256;
 constexpr int kSmallMaxM = 64;
 constexpr int kSmallMaxElems = 4096;
 
-struct SmallArgs {
+struct SmallBank {
     const uint16_t* x0;     // input slots [batch][rows][cols], bf16 bits (unscaled)
     uint16_t* dest;         // output slots, same layout (may equal x0)
     const float* scale;
     const int* live;
     int rows, cols, m, n;
-    bool tall;
+    int tall;
+    int first_slot;         // the bank's first workgroup in the launch
+};
+
+struct SmallArgs {
+    SmallBank bank[kMaxSmallBanks];
+    int nbanks;
     int steps;
     float coef[kMaxRounds][3];
 };
 
 __device__ __forceinline__ float round_bf16(float y) { return bf16_to_f32(f32_to_bf16_rne(y)); }
 
-__global__ void __launch_bounds__(kSmallThreads) ns_small_kernel(SmallArgs p) {
+__global__ void __launch_bounds__(kSmallThreads) ns_small_kernel(SmallArgs args) {
     extern __shared__ float sm[];
+    int bi = 0;
+    for (int i = 1; i < args.nbanks; ++i)
+        if ((int)blockIdx.x >= args.bank[i].first_slot) bi = i;
+    const SmallBank& p = args.bank[__builtin_amdgcn_readfirstlane(bi)];
     const int m = p.m, n = p.n, mn = m * n, mm = m * m;
     float* X = sm;                 // [m][n]
     float* Y = X + mn;             // [m][n], next round
     float* A = Y + mn;             // [m][m]
     float* B = A + mm;             // [m][m]
-    const int slot = blockIdx.x;
+    const int slot = (int)blockIdx.x - p.first_slot;
     const int tid = threadIdx.x;
     const uint16_t* src = p.x0 + (int64_t)slot * mn;
     uint16_t* dst = p.dest + (int64_t)slot * mn;
@@ -63,8 +73,8 @@ __global__ void __launch_bounds__(kSmallThreads) ns_small_kernel(SmallArgs p) {
     }
     const float s = p.scale[slot];
     __syncthreads();
-    for (int t = 0; t < p.steps; ++t) {
-        const float a = p.coef[t][0], b = p.coef[t][1], c = p.coef[t][2];
+    for (int t = 0; t < args.steps; ++t) {
+        const float a = args.coef[t][0], b = args.coef[t][1], c = args.coef[t][2];
         const float sig_a = t == 0 ? s * s : 1.f, sig_x = t == 0 ? s : 1.f;
         for (int e = tid; e < mm; e += kSmallThreads) {
             const int i = e / m, j = e - i * m;
@@ -107,26 +117,41 @@ bool ns_small_eligible(int64_t rows, int64_t cols, int steps) {
     return steps >= 1 && steps <= kMaxRounds && m <= kSmallMaxM && rows * cols <= kSmallMaxElems;
 }
 
-hipError_t ns_small(const NsSmall& r, hipStream_t stream) {
-    SmallArgs p{};
-    p.x0 = r.x0;
-    p.dest = r.dest;
-    p.scale = r.scale;
-    p.live = r.live;
-    p.rows = (int)r.rows;
-    p.cols = (int)r.cols;
-    p.tall = r.rows > r.cols;
-    p.m = (int)(p.tall ? r.cols : r.rows);
-    p.n = (int)(p.tall ? r.rows : r.cols);
-    p.steps = r.steps;
-    for (int t = 0; t < r.steps && t < kMaxRounds; ++t) {
-        p.coef[t][0] = r.coef[t].a;
-        p.coef[t][1] = r.coef[t].b;
-        p.coef[t][2] = r.coef[t].c;
+hipError_t ns_small(const NsSmall* banks, int nbanks, int steps, const NsCoef* coef, hipStream_t stream) {
+    if (steps < 1 || steps > kMaxRounds) return hipErrorInvalidValue;
+    for (int i0 = 0; i0 < nbanks; i0 += kMaxSmallBanks) {
+        SmallArgs p{};
+        p.nbanks = nbanks - i0 < kMaxSmallBanks ? nbanks - i0 : kMaxSmallBanks;
+        p.steps = steps;
+        for (int t = 0; t < steps; ++t) {
+            p.coef[t][0] = coef[t].a;
+            p.coef[t][1] = coef[t].b;
+            p.coef[t][2] = coef[t].c;
+        }
+        int slots = 0;
+        size_t lds = 0;
+        for (int j = 0; j < p.nbanks; ++j) {
+            const NsSmall& r = banks[i0 + j];
+            SmallBank& b = p.bank[j];
+            b.x0 = r.x0;
+            b.dest = r.dest;
+            b.scale = r.scale;
+            b.live = r.live;
+            b.rows = (int)r.rows;
+            b.cols = (int)r.cols;
+            b.tall = r.rows > r.cols ? 1 : 0;
+            b.m = (int)(b.tall ? r.cols : r.rows);
+            b.n = (int)(b.tall ? r.rows : r.cols);
+            b.first_slot = slots;
+            slots += (int)r.batch;
+            const size_t need = (size_t)(2 * b.m * b.n + 2 * b.m * b.m) * sizeof(float);
+            lds = need > lds ? need : lds;
+        }
+        ns_small_kernel<<<dim3((unsigned)slots), kSmallThreads, lds, stream>>>(p);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    const size_t lds = (size_t)(2 * p.m * p.n + 2 * p.m * p.m) * sizeof(float);
-    ns_small_kernel<<<dim3((unsigned)r.batch), kSmallThreads, lds, stream>>>(p);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace mb

@@ -4,6 +4,13 @@
 //   * partial sums of x^2 for a stand-alone Newton-Schulz call;
 //   * the per-slot scale s = 1 / (||u||_F + eps) and live flag;
 //   * the mixed-precision apply on bf16 weight + uint16 low mantissa.
+// Momentum, scale and apply each take up to kMaxStreamBanks banks in one
+// launch: the launch's workgroups are numbered bank after bank, and each
+// workgroup finds its bank, slot and chunk from that numbering.  Per-slot
+// scalars (mu, nu, decay, eta) come from the bank's own values or, if given,
+// from one float32 device table with a row per slot of the call (every bank's
+// step scalars in one buffer that a graph replay reads, as the "Unified
+// zero-copy optimizer and transposed LM head" page, section 4, keeps them).
 //
 // Momentum follows the two lerps of "Muon Custom Sizing", section 4
 // (buf' = mu*buf + (1-mu)*g, then u = (1-mu)*g + mu*buf'); the apply follows
@@ -15,6 +22,40 @@
 #include "kernels.hpp"
 
 namespace mb {
+
+namespace {
+
+// One bank of a multi-bank launch, as the kernels see it (momentum uses grad..partials, the apply
+// w_hi..lr_mul_per_slot); its workgroups are [first_block, first_block + batch * nchunks).
+struct StreamBank {
+    const void* grad;
+    void* buf;
+    uint16_t* u;
+    double* partials;
+    uint16_t* w_hi;
+    uint16_t* w_lo;
+    const uint16_t* v;
+    const float* lr_mul_per_slot;
+    int64_t slot_numel;
+    int64_t first_block;
+    int nchunks, batch, slot_base;
+    int f32, vec;
+    float mu, nu, decay, eta;
+};
+
+struct StreamArgs {
+    StreamBank bank[kMaxStreamBanks];
+    int nbanks;
+    const f32x4* slot_scalars;      // NULL, or (mu, nu, decay, eta) per slot of the call
+};
+
+struct ScaleArgs {
+    ScaleBank bank[kMaxStreamBanks];
+    int nbanks;
+    double eps;
+};
+
+}  // namespace
 
 // ---------------------------------------------------------------------------
 // momentum + Nesterov
@@ -58,15 +99,14 @@ __device__ __forceinline__ double block_sum256(double v, double* red) {
     return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
+// One chunk of one slot: buf' and u of its elements, and their sum of u^2 (returned in every thread).
 template <bool F32, bool VEC>
-__global__ void __launch_bounds__(256) momentum_kernel(const void* __restrict__ grad_, void* __restrict__ buf_,
-                                                       uint16_t* __restrict__ u, double* __restrict__ partials,
-                                                       int64_t slot_numel, int64_t chunk_elems, float mu, float nu) {
-    const int64_t slot = blockIdx.y;
-    const int64_t chunk = blockIdx.x;
+__device__ __forceinline__ double momentum_chunk(const void* __restrict__ grad_, void* __restrict__ buf_,
+                                                 uint16_t* __restrict__ u, int64_t slot, int64_t chunk,
+                                                 int64_t slot_numel, float mu, float nu, double* red) {
     const int64_t base = slot * slot_numel;
-    const int64_t lo = chunk * chunk_elems;
-    const int64_t hi = min(lo + chunk_elems, slot_numel);
+    const int64_t lo = chunk * kStreamChunk;
+    const int64_t hi = min(lo + kStreamChunk, slot_numel);
     double acc = 0.0;
     if (VEC) {
         // 8 consecutive elements per thread per step; slot_numel % 8 == 0 and bases are 16-byte aligned
@@ -133,9 +173,38 @@ __global__ void __launch_bounds__(256) momentum_kernel(const void* __restrict__ 
             u[idx] = ub;
         }
     }
+    return block_sum256(acc, red);
+}
+
+// The bank of workgroup `blk` in a multi-bank launch (banks in increasing first_block; wave-uniform).
+__device__ __forceinline__ int find_bank(const StreamArgs& p, int64_t blk) {
+    int b = 0;
+    for (int i = 1; i < p.nbanks; ++i)
+        if (blk >= p.bank[i].first_block) b = i;
+    return __builtin_amdgcn_readfirstlane(b);
+}
+
+__global__ void __launch_bounds__(256) momentum_kernel(StreamArgs p) {
+    const int64_t blk = blockIdx.x;
+    const StreamBank& bk = p.bank[find_bank(p, blk)];
+    const int64_t local = blk - bk.first_block;
+    const int64_t slot = local / bk.nchunks, chunk = local - slot * bk.nchunks;
+    float mu = bk.mu, nu = bk.nu;
+    if (p.slot_scalars) {
+        const f32x4 sc = p.slot_scalars[bk.slot_base + slot];
+        mu = sc[0];
+        nu = sc[1];
+    }
     __shared__ double red[4];
-    acc = block_sum256(acc, red);
-    if (threadIdx.x == 0 && partials) partials[slot * gridDim.x + chunk] = acc;
+    double sum;
+    if (bk.f32) {
+        sum = bk.vec ? momentum_chunk<true, true>(bk.grad, bk.buf, bk.u, slot, chunk, bk.slot_numel, mu, nu, red)
+                     : momentum_chunk<true, false>(bk.grad, bk.buf, bk.u, slot, chunk, bk.slot_numel, mu, nu, red);
+    } else {
+        sum = bk.vec ? momentum_chunk<false, true>(bk.grad, bk.buf, bk.u, slot, chunk, bk.slot_numel, mu, nu, red)
+                     : momentum_chunk<false, false>(bk.grad, bk.buf, bk.u, slot, chunk, bk.slot_numel, mu, nu, red);
+    }
+    if (threadIdx.x == 0 && bk.partials) bk.partials[slot * bk.nchunks + chunk] = sum;
 }
 
 // ---------------------------------------------------------------------------
@@ -181,22 +250,23 @@ constexpr int kFoldMinExp = -45;
 constexpr int kFoldMaxExp = 60;
 constexpr int kScaleParts = 4;          // workgroups per slot (they share the copy of a pre-scaled slot)
 
-__global__ void __launch_bounds__(256) ns_scale_kernel(const double* __restrict__ partials, int nchunks, double eps,
-                                                       float* __restrict__ scale, int* __restrict__ live,
-                                                       int* __restrict__ heads, int* __restrict__ ctr,
-                                                       const uint16_t* __restrict__ x0, uint16_t* __restrict__ xpre,
-                                                       int64_t slot_numel) {
-    const int slot = blockIdx.x;
+__global__ void __launch_bounds__(256) ns_scale_kernel(ScaleArgs p) {
+    const int gslot = blockIdx.x;
+    int b = 0;
+    for (int i = 1; i < p.nbanks; ++i)
+        if (gslot >= p.bank[i].first_slot) b = i;
+    const ScaleBank& bk = p.bank[__builtin_amdgcn_readfirstlane(b)];
+    const int slot = gslot - bk.first_slot;
     const int part = blockIdx.y;
     const int tid = threadIdx.x;
     // persistent kernel state: queue heads, error word and exit count, and this slot's counter
     if (part == 0) {
-        if (heads && slot == 0 && tid < 32) heads[tid] = 0;
-        if (ctr && tid == 0) ctr[slot] = 0;
+        if (bk.heads && slot == 0 && tid < 32) bk.heads[tid] = 0;
+        if (bk.ctr && tid == 0) bk.ctr[slot] = 0;
     }
     // every workgroup of the slot forms the same sum in the same order
     double acc = 0.0;
-    for (int i = tid; i < nchunks; i += 256) acc += partials[(int64_t)slot * nchunks + i];
+    for (int i = tid; i < bk.nchunks; i += 256) acc += bk.partials[(int64_t)slot * bk.nchunks + i];
     __shared__ double red[4];
     __shared__ int s_word;
     acc = block_sum256(acc, red);
@@ -208,27 +278,27 @@ __global__ void __launch_bounds__(256) ns_scale_kernel(const double* __restrict_
             const int e = ilogb(nrm);
             if (e >= kFoldMinExp && e < kFoldMaxExp) {
                 word = kLiveBit;
-                sc = (float)(1.0 / (nrm + eps));
+                sc = (float)(1.0 / (nrm + p.eps));
             } else {
                 const int k = -e;
                 word = kLiveBit | kPrescaledBit | ((k + kPrescaleBias) << kPrescaleShift);
-                sc = (float)(ldexp(1.0, -k) / (nrm + eps));
+                sc = (float)(ldexp(1.0, -k) / (nrm + p.eps));
             }
         }
         s_word = word;
         if (part == 0) {
-            scale[slot] = sc;
-            live[slot] = word;
+            bk.scale[slot] = sc;
+            bk.live[slot] = word;
         }
     }
     __syncthreads();
     const int word = s_word;
     if (!(word & kPrescaledBit)) return;
     const int k = prescale_exp(word);
-    const uint16_t* src = x0 + (int64_t)slot * slot_numel;
-    uint16_t* dst = xpre + (int64_t)slot * slot_numel;
-    const int64_t per = (slot_numel + kScaleParts - 1) / kScaleParts;
-    const int64_t lo = (int64_t)part * per, hi = min(lo + per, slot_numel);
+    const uint16_t* src = bk.x0 + (int64_t)slot * bk.slot_numel;
+    uint16_t* dst = bk.xpre + (int64_t)slot * bk.slot_numel;
+    const int64_t per = (bk.slot_numel + kScaleParts - 1) / kScaleParts;
+    const int64_t lo = (int64_t)part * per, hi = min(lo + per, bk.slot_numel);
     // exact: |X0| < 2, and only elements below 2^-126 of the norm can lose bits
     for (int64_t e = lo + tid; e < hi; e += 256) dst[e] = f32_to_bf16_rne(ldexpf(bf16_to_f32(src[e]), k));
 }
@@ -244,17 +314,14 @@ __device__ __forceinline__ uint32_t apply_elem(uint32_t hi, uint32_t lo, uint32_
     return __float_as_uint(r);
 }
 
-// VEC: 8 elements per thread per step (slot_numel % 8 == 0, 16-byte aligned bases).
-template <bool VEC, bool PER_SLOT>
-__global__ void __launch_bounds__(256) apply_kernel(uint16_t* __restrict__ w_hi, uint16_t* __restrict__ w_lo,
-                                                    const uint16_t* __restrict__ v, int64_t slot_numel,
-                                                    int64_t chunk_elems, float eta, float decay,
-                                                    const float* __restrict__ lr_mul_per_slot) {
-    const int64_t slot = blockIdx.y;
+// One chunk of one slot.  VEC: 8 elements per thread per step (slot_numel % 8 == 0, 16-byte aligned bases).
+template <bool VEC>
+__device__ __forceinline__ void apply_chunk(uint16_t* __restrict__ w_hi, uint16_t* __restrict__ w_lo,
+                                            const uint16_t* __restrict__ v, int64_t slot, int64_t chunk,
+                                            int64_t slot_numel, float eta, float decay) {
     const int64_t base = slot * slot_numel;
-    const int64_t lo = (int64_t)blockIdx.x * chunk_elems;
-    const int64_t hi = min(lo + chunk_elems, slot_numel);
-    const float eta_s = PER_SLOT ? __fmul_rn(eta, lr_mul_per_slot[slot]) : eta;
+    const int64_t lo = chunk * kStreamChunk;
+    const int64_t hi = min(lo + kStreamChunk, slot_numel);
     if (VEC) {
         for (int64_t e = lo + (int64_t)threadIdx.x * 8; e < hi; e += 256 * 8) {
             const int64_t idx = base + e;
@@ -264,8 +331,8 @@ __global__ void __launch_bounds__(256) apply_kernel(uint16_t* __restrict__ w_hi,
             u32x4 ho, lo2;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                uint32_t r0 = apply_elem(h[q] & 0xFFFFu, l[q] & 0xFFFFu, vv[q] & 0xFFFFu, eta_s, decay);
-                uint32_t r1 = apply_elem(h[q] >> 16, l[q] >> 16, vv[q] >> 16, eta_s, decay);
+                uint32_t r0 = apply_elem(h[q] & 0xFFFFu, l[q] & 0xFFFFu, vv[q] & 0xFFFFu, eta, decay);
+                uint32_t r1 = apply_elem(h[q] >> 16, l[q] >> 16, vv[q] >> 16, eta, decay);
                 ho[q] = (r0 >> 16) | (r1 & 0xFFFF0000u);
                 lo2[q] = (r0 & 0xFFFFu) | (r1 << 16);
             }
@@ -275,74 +342,125 @@ __global__ void __launch_bounds__(256) apply_kernel(uint16_t* __restrict__ w_hi,
     } else {
         for (int64_t e = lo + threadIdx.x; e < hi; e += 256) {
             const int64_t idx = base + e;
-            uint32_t r = apply_elem(w_hi[idx], w_lo[idx], v[idx], eta_s, decay);
+            uint32_t r = apply_elem(w_hi[idx], w_lo[idx], v[idx], eta, decay);
             w_hi[idx] = (uint16_t)(r >> 16);
             w_lo[idx] = (uint16_t)(r & 0xFFFFu);
         }
     }
 }
 
+__global__ void __launch_bounds__(256) apply_kernel(StreamArgs p) {
+    const int64_t blk = blockIdx.x;
+    const StreamBank& bk = p.bank[find_bank(p, blk)];
+    const int64_t local = blk - bk.first_block;
+    const int64_t slot = local / bk.nchunks, chunk = local - slot * bk.nchunks;
+    float eta = bk.eta, decay = bk.decay;
+    if (p.slot_scalars) {
+        const f32x4 sc = p.slot_scalars[bk.slot_base + slot];
+        decay = sc[2];
+        eta = sc[3];
+    } else if (bk.lr_mul_per_slot) {
+        eta = __fmul_rn(eta, bk.lr_mul_per_slot[slot]);
+    }
+    if (bk.vec) apply_chunk<true>(bk.w_hi, bk.w_lo, bk.v, slot, chunk, bk.slot_numel, eta, decay);
+    else apply_chunk<false>(bk.w_hi, bk.w_lo, bk.v, slot, chunk, bk.slot_numel, eta, decay);
+}
+
 // ---------------------------------------------------------------------------
 // host-side launchers
 // ---------------------------------------------------------------------------
 
-// Elements per workgroup of the streaming kernels (and per partial sum of u^2): 4096 is two 8-element
-// groups per thread, so that enough short workgroups are in flight to overlap the momentum's binary64
-// arithmetic with its memory traffic (16384 per workgroup measured 9 % slower for momentum, 4 % for
-// the apply).
-int64_t stream_chunk_elems(bool) { return 4096; }
-
-int stream_chunks(int64_t slot_numel, bool vec) {
-    // fixed chunks of stream_chunk_elems() elements (a multiple of 8), so every
-    // thread's 8-element group stays inside one slot and one chunk
-    const int64_t per = stream_chunk_elems(vec);
-    int64_t n = (slot_numel + per - 1) / per;
+int stream_chunks(int64_t slot_numel) {
+    // fixed chunks of kStreamChunk elements (a multiple of 8), so every thread's 8-element group stays
+    // inside one slot and one chunk
+    int64_t n = (slot_numel + kStreamChunk - 1) / kStreamChunk;
     return (int)(n < 1 ? 1 : n);
 }
 
-hipError_t launch_momentum(const void* grad, void* buf, uint16_t* u, double* partials, int64_t batch,
-                           int64_t slot_numel, bool f32, bool vec, float mu, float nu, hipStream_t stream) {
-    const int64_t chunk = stream_chunk_elems(vec);
-    dim3 grid((unsigned)stream_chunks(slot_numel, vec), (unsigned)batch);
-    if (f32) {
-        if (vec) momentum_kernel<true, true><<<grid, 256, 0, stream>>>(grad, buf, u, partials, slot_numel, chunk, mu, nu);
-        else momentum_kernel<true, false><<<grid, 256, 0, stream>>>(grad, buf, u, partials, slot_numel, chunk, mu, nu);
-    } else {
-        if (vec) momentum_kernel<false, true><<<grid, 256, 0, stream>>>(grad, buf, u, partials, slot_numel, chunk, mu, nu);
-        else momentum_kernel<false, false><<<grid, 256, 0, stream>>>(grad, buf, u, partials, slot_numel, chunk, mu, nu);
+namespace {
+
+// Banks [i, i + count) of one launch: their workgroups numbered bank after bank.
+template <class Fill>
+hipError_t launch_streams(int nbanks, const float* slot_scalars, hipStream_t stream, Fill fill,
+                          void (*kernel)(StreamArgs)) {
+    for (int i0 = 0; i0 < nbanks; i0 += kMaxStreamBanks) {
+        StreamArgs p{};
+        p.nbanks = nbanks - i0 < kMaxStreamBanks ? nbanks - i0 : kMaxStreamBanks;
+        p.slot_scalars = reinterpret_cast<const f32x4*>(slot_scalars);
+        int64_t blocks = 0;
+        for (int j = 0; j < p.nbanks; ++j) {
+            StreamBank& b = p.bank[j];
+            fill(i0 + j, b);
+            b.nchunks = stream_chunks(b.slot_numel);
+            b.first_block = blocks;
+            blocks += (int64_t)b.batch * b.nchunks;
+        }
+        if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_momentum(const MomentumBank* banks, int nbanks, const float* slot_scalars, hipStream_t stream) {
+    return launch_streams(nbanks, slot_scalars, stream, [&](int i, StreamBank& b) {
+        const MomentumBank& m = banks[i];
+        b.grad = m.grad;
+        b.buf = m.buf;
+        b.u = m.u;
+        b.partials = m.partials;
+        b.slot_numel = m.slot_numel;
+        b.batch = (int)m.batch;
+        b.slot_base = m.slot_base;
+        b.f32 = m.f32 ? 1 : 0;
+        b.vec = m.slot_numel % 8 == 0 ? 1 : 0;
+        b.mu = m.mu;
+        b.nu = m.nu;
+    }, momentum_kernel);
+}
+
+hipError_t launch_apply(const ApplyBank* banks, int nbanks, const float* slot_scalars, hipStream_t stream) {
+    return launch_streams(nbanks, slot_scalars, stream, [&](int i, StreamBank& b) {
+        const ApplyBank& a = banks[i];
+        b.w_hi = a.w_hi;
+        b.w_lo = a.w_lo;
+        b.v = a.v;
+        b.lr_mul_per_slot = a.lr_mul_per_slot;
+        b.slot_numel = a.slot_numel;
+        b.batch = (int)a.batch;
+        b.slot_base = a.slot_base;
+        b.vec = a.slot_numel % 8 == 0 ? 1 : 0;
+        b.eta = a.eta;
+        b.decay = a.decay;
+    }, apply_kernel);
+}
+
+hipError_t launch_sumsq(const uint16_t* x, double* partials, int64_t batch, int64_t slot_numel, hipStream_t stream) {
+    dim3 grid((unsigned)stream_chunks(slot_numel), (unsigned)batch);
+    if (slot_numel % 8 == 0) sumsq_kernel<true><<<grid, 256, 0, stream>>>(x, partials, slot_numel, kStreamChunk);
+    else sumsq_kernel<false><<<grid, 256, 0, stream>>>(x, partials, slot_numel, kStreamChunk);
     return hipGetLastError();
 }
 
-hipError_t launch_sumsq(const uint16_t* x, double* partials, int64_t batch, int64_t slot_numel, bool vec,
-                        hipStream_t stream) {
-    const int64_t chunk = stream_chunk_elems(vec);
-    dim3 grid((unsigned)stream_chunks(slot_numel, vec), (unsigned)batch);
-    if (vec) sumsq_kernel<true><<<grid, 256, 0, stream>>>(x, partials, slot_numel, chunk);
-    else sumsq_kernel<false><<<grid, 256, 0, stream>>>(x, partials, slot_numel, chunk);
-    return hipGetLastError();
-}
-
-hipError_t launch_ns_scale(const double* partials, int nchunks, int64_t batch, double eps, float* scale, int* live,
-                           int* heads, int* ctr, const uint16_t* x0, uint16_t* xpre, int64_t slot_numel,
-                           hipStream_t stream) {
-    ns_scale_kernel<<<dim3((unsigned)batch, kScaleParts), 256, 0, stream>>>(partials, nchunks, eps, scale, live, heads,
-                                                                             ctr, x0, xpre, slot_numel);
-    return hipGetLastError();
-}
-
-hipError_t launch_apply(uint16_t* w_hi, uint16_t* w_lo, const uint16_t* v, int64_t batch, int64_t slot_numel,
-                        bool vec, float eta, float decay, const float* lr_mul_per_slot, hipStream_t stream) {
-    const int64_t chunk = stream_chunk_elems(vec);
-    dim3 grid((unsigned)stream_chunks(slot_numel, vec), (unsigned)batch);
-    if (lr_mul_per_slot) {
-        if (vec) apply_kernel<true, true><<<grid, 256, 0, stream>>>(w_hi, w_lo, v, slot_numel, chunk, eta, decay, lr_mul_per_slot);
-        else apply_kernel<false, true><<<grid, 256, 0, stream>>>(w_hi, w_lo, v, slot_numel, chunk, eta, decay, lr_mul_per_slot);
-    } else {
-        if (vec) apply_kernel<true, false><<<grid, 256, 0, stream>>>(w_hi, w_lo, v, slot_numel, chunk, eta, decay, nullptr);
-        else apply_kernel<false, false><<<grid, 256, 0, stream>>>(w_hi, w_lo, v, slot_numel, chunk, eta, decay, nullptr);
+hipError_t launch_ns_scale(const ScaleBank* banks, int nbanks, double eps, hipStream_t stream) {
+    for (int i0 = 0; i0 < nbanks; i0 += kMaxStreamBanks) {
+        ScaleArgs p{};
+        p.nbanks = nbanks - i0 < kMaxStreamBanks ? nbanks - i0 : kMaxStreamBanks;
+        p.eps = eps;
+        int slots = 0;
+        for (int j = 0; j < p.nbanks; ++j) {
+            p.bank[j] = banks[i0 + j];
+            p.bank[j].first_slot = slots;
+            slots += (int)banks[i0 + j].batch;
+        }
+        ns_scale_kernel<<<dim3((unsigned)slots, kScaleParts), 256, 0, stream>>>(p);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace mb

@@ -229,3 +229,39 @@ def test_noalloc_rejects_oversized_shapes_before_touching_the_device(L):
     assert L.ns_orthogonalize_batched_noalloc(p, p + (1 << 30), *big, 5, 3.4445, -4.775, 2.0315, 1e-7, None) == WORKSPACE
     assert b"static scratch" in L.mb_last_error()
     assert L.ns_orthogonalize_batched_noalloc(p, p + (1 << 30), 0, 768, 768, 5, 3.4445, -4.775, 2.0315, 1e-7, None) == SHAPE
+
+
+def test_slot_scalars_fill_is_the_call_scalars(L):
+    """The host table holds, per slot in bank order, the float32 (mu, nu, decay, eta) the step derives
+    from the hyper-parameters and each bank's multipliers; the oracle's step_scalars gives the same
+    values."""
+    import numpy as np
+    import oracle
+    b1, _ = _bank(batch=3, rows=64, cols=32)
+    b2, _ = _bank(batch=2, rows=16, cols=64, base=1 << 40)
+    b2.lr_mul, b2.wd_mul = 1.5, 0.5
+    hp = api.make_hparams(lr=0.05, weight_decay=0.1, momentum=0.9)
+    arr = (api.mb_bank * 2)(b1, b2)
+    out = np.zeros((5, 4), dtype=np.float32)
+    assert L.mb_slot_scalars_fill(arr, 2, ctypes.byref(hp), out.ctypes.data, out.size) == OK
+    for rows, (r, c, lm, wm) in zip((range(0, 3), range(3, 5)), ((64, 32, 1.0, 1.0), (16, 64, 1.5, 0.5))):
+        sc = oracle.step_scalars(0.05, 0.1, 0.9, r, c, lr_mul=lm, wd_mul=wm)
+        for i in rows:
+            assert tuple(out[i].astype(np.float64)) == (sc.mu, sc.nu, sc.decay, sc.eta)
+    assert L.mb_slot_scalars_fill(arr, 2, ctypes.byref(hp), out.ctypes.data, out.size - 1) == WORKSPACE
+    b3, _ = _bank(lr_mul_per_slot=1 << 44)
+    assert L.mb_slot_scalars_fill((api.mb_bank * 1)(b3), 1, None, out.ctypes.data, out.size) == VALUE
+    assert L.mb_slot_scalars_fill(None, 1, None, out.ctypes.data, out.size) == NULL
+
+
+def test_step_with_slot_scalars_validation(L):
+    good, ws = _bank()
+    need = L.mb_step_workspace_bytes((api.mb_bank * 1)(good), 1)
+    hp = api.default_hparams()
+    hp.slot_scalars = (1 << 46) + 8
+    assert _step(L, [good], ws, need, hp) == ALIGN
+    hp.slot_scalars = good.grad + 64
+    assert _step(L, [good], ws, need, hp) == ALIAS
+    hp.slot_scalars = 1 << 46
+    assert _step(L, [_bank(lr_mul_per_slot=1 << 44)[0]], ws, need, hp) == VALUE
+    assert b"lr_mul_per_slot" in L.mb_last_error()

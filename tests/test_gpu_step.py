@@ -176,6 +176,60 @@ def _check_paths_bitwise(config, banks0):
     say(f"  {checked} persistent banks bit-identical to one launch per contraction on every slot")
 
 
+def test_slot_scalar_table_matches_oracle():
+    """Workload 3 (attention, MLP and both gate banks) with a per-slot table whose momentum, decay and
+    learning rate differ from slot to slot: momentum and u bit-exact against the oracle with each slot's
+    own scalars, the apply bit-exact on the GPU's v, Newton-Schulz within the tolerance on sampled slots."""
+    say("bank step with a per-slot scalar table")
+    config = 3
+    specs, host = CONFIGS[config], host_inputs(config)
+    banks = _upload(config)
+    table = api.slot_scalars_table(banks)
+    rng = np.random.default_rng(123)
+    mu = rng.uniform(0.8, 0.99, table.shape[0])
+    table[:, 0] = mu.astype(np.float32)
+    table[:, 1] = (1.0 - mu).astype(np.float32)
+    table[:, 2] = rng.uniform(0.99, 1.0, table.shape[0]).astype(np.float32)
+    table[:, 3] = (table[:, 3] * rng.uniform(0.5, 2.0, table.shape[0])).astype(np.float32)
+    api.muon_bank_step(banks, api.with_slot_scalars(None, torch.from_numpy(table).cuda()))
+    torch.cuda.synchronize()
+    row = 0
+    for spec, h, b in zip(specs, host, banks):
+        tab = table[row:row + spec.batch].astype(np.float64)
+        row += spec.batch
+        mu_s, nu_s, d_s, eta_s = (tab[:, k][:, None, None] for k in range(4))
+        want_buf, want_u = oracle.momentum_nesterov(vals(h["grad"]), vals(h["momentum"]), mu_s, nu_s, oracle.BF16)
+        np.testing.assert_array_equal(vals(bits(b.momentum)), want_buf, err_msg=f"{spec.name} momentum")
+        u = bits(b.u_out)
+        np.testing.assert_array_equal(vals(u), want_u, err_msg=f"{spec.name} u")
+        v = bits(b.v_out)
+        hi, lo = oracle.mp_apply_update(h["w_hi"], h["w_lo"], vals(v), eta_s, d_s)
+        np.testing.assert_array_equal(bits(b.w_hi), hi, err_msg=f"{spec.name} w_hi")
+        np.testing.assert_array_equal(bits(b.w_lo), lo, err_msg=f"{spec.name} w_lo")
+        live = list(spec.live_slots)
+        ns = live[:2] + live[-1:]
+        err = rel_fro(vals(v[ns]), oracle.newton_schulz(vals(u[ns])))
+        assert np.all(err <= NS_TOL), err
+
+
+def test_124m_step_is_five_launches():
+    """The 124M model's whole step (attention, MLP and two gate banks) enqueues five kernels: momentum of
+    every bank, their scales, the persistent Newton-Schulz launch, the gates' Newton-Schulz, every apply."""
+    say("launch count")
+    banks = _upload(3)
+    ws = torch.empty(api.mb_step_workspace_bytes(banks), dtype=torch.uint8, device="cuda")
+    api.muon_bank_step(banks, workspace=ws)
+    torch.cuda.synchronize()
+    api.mb_timing_enable(True)
+    api.mb_timing_read()
+    api.muon_bank_step(banks, workspace=ws)
+    torch.cuda.synchronize()
+    counts = {k: n for k, (n, _) in api.mb_timing_read().items()}
+    api.mb_timing_enable(False)
+    say(f"  launches {counts}")
+    assert counts == {"momentum": 1, "ns_scale": 1, "ns_persist": 1, "ns_small": 1, "apply": 1}
+
+
 def test_bank_step_is_deterministic():
     say("bank step determinism")
     outs = []
