@@ -25,7 +25,7 @@ extern "C" {
  * 1..65535), MB_ERR_ALIGN, MB_ERR_HIP. */
 mb_status mb_probe_mfma_bf16(int64_t iters, int32_t workgroups, float *sink, void *stream);
 
-/* dst[0, bytes) = src[0, bytes) with 16-byte loads and stores, four per thread, all loads first (device
+/* dst[0, bytes) = src[0, bytes) with 16-byte non-temporal loads and stores, four per thread, all loads first (device
  * buffers, 16-byte aligned, not overlapping; bytes a positive multiple of 16): 2 * bytes of HBM traffic
  * per launch once the buffers exceed the caches.  MB_ERR_NULL, MB_ERR_SHAPE, MB_ERR_ALIGN, MB_ERR_ALIAS, MB_ERR_HIP. */
 mb_status mb_probe_copy(void *dst, const void *src, int64_t bytes, void *stream);

@@ -18,6 +18,7 @@ struct RoundTimer {
 // per thread of 256, so that many short workgroups are in flight (16384 per workgroup measured 9 %
 // slower for momentum, 4 % for the apply).
 constexpr int64_t kStreamChunk = 4096;
+constexpr int kStreamGroups = (int)(kStreamChunk / (256 * 8));   // 8-element groups per thread and chunk
 // Banks per launch of the streaming kernels (momentum, scale, apply); more take several launches.
 constexpr int kMaxStreamBanks = 16;
 int stream_chunks(int64_t slot_numel);

@@ -49,12 +49,12 @@ __global__ void __launch_bounds__(256) copy_probe_kernel(const u32x4* __restrict
 #pragma unroll
     for (int j = 0; j < kCopyVecs; ++j) {
         const int64_t i = base + (int64_t)j * 256;
-        if (i < n16) v[j] = src[i];
+        if (i < n16) v[j] = __builtin_nontemporal_load(src + i);
     }
 #pragma unroll
     for (int j = 0; j < kCopyVecs; ++j) {
         const int64_t i = base + (int64_t)j * 256;
-        if (i < n16) dst[i] = v[j];
+        if (i < n16) __builtin_nontemporal_store(v[j], dst + i);
     }
 }
 

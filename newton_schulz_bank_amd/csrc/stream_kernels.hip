@@ -99,8 +99,20 @@ __device__ __forceinline__ double block_sum256(double v, double* red) {
     return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
+// 16-byte load / store, non-temporal when NT (streams larger than the last-level cache: nothing to keep).
+template <bool NT>
+__device__ __forceinline__ u32x4 ld16(const u32x4* p) {
+    if (NT) return __builtin_nontemporal_load(p);
+    return *p;
+}
+template <bool NT>
+__device__ __forceinline__ void st16(u32x4* p, u32x4 v) {
+    if (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
 // One chunk of one slot: buf' and u of its elements, and their sum of u^2 (returned in every thread).
-template <bool F32, bool VEC>
+template <bool F32, bool VEC, bool NT>
 __device__ __forceinline__ double momentum_chunk(const void* __restrict__ grad_, void* __restrict__ buf_,
                                                  uint16_t* __restrict__ u, int64_t slot, int64_t chunk,
                                                  int64_t slot_numel, float mu, float nu, double* red) {
@@ -108,7 +120,42 @@ __device__ __forceinline__ double momentum_chunk(const void* __restrict__ grad_,
     const int64_t lo = chunk * kStreamChunk;
     const int64_t hi = min(lo + kStreamChunk, slot_numel);
     double acc = 0.0;
-    if (VEC) {
+    if (VEC && !F32 && NT) {
+        // a stream larger than the last-level cache: both 8-element groups of this thread (a chunk is
+        // kStreamGroups groups of 256 x 8 elements) loaded before the first store, the loads and the store
+        // of buf' (which the step does not read again) non-temporal; u, which the Newton-Schulz launch
+        // reads next, stored normally.  slot_numel % 8 == 0 and bases are 16-byte aligned.
+        u32x4 gv[kStreamGroups], bv[kStreamGroups];
+#pragma unroll
+        for (int k = 0; k < kStreamGroups; ++k) {
+            const int64_t e = lo + (int64_t)threadIdx.x * 8 + (int64_t)k * 256 * 8;
+            if (e < hi) {
+                gv[k] = ld16<NT>(reinterpret_cast<const u32x4*>((const uint16_t*)grad_ + base + e));
+                bv[k] = ld16<NT>(reinterpret_cast<const u32x4*>((const uint16_t*)buf_ + base + e));
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kStreamGroups; ++k) {
+            const int64_t e = lo + (int64_t)threadIdx.x * 8 + (int64_t)k * 256 * 8;
+            if (e >= hi) continue;
+            u32x4 bo, uo;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float bn32[2], uv[2];
+                uint16_t bn16[2], ub[2];
+                momentum_elem(__uint_as_float(gv[k][q] << 16), __uint_as_float(bv[k][q] << 16), mu, nu, bn32[0],
+                              bn16[0], ub[0], false, uv[0]);
+                momentum_elem(__uint_as_float(gv[k][q] & 0xFFFF0000u), __uint_as_float(bv[k][q] & 0xFFFF0000u), mu, nu,
+                              bn32[1], bn16[1], ub[1], false, uv[1]);
+                acc = add_sq(acc, uv[0]);
+                acc = add_sq(acc, uv[1]);
+                bo[q] = (uint32_t)bn16[0] | ((uint32_t)bn16[1] << 16);
+                uo[q] = (uint32_t)ub[0] | ((uint32_t)ub[1] << 16);
+            }
+            st16<NT>(reinterpret_cast<u32x4*>((uint16_t*)buf_ + base + e), bo);
+            *reinterpret_cast<u32x4*>(u + base + e) = uo;
+        }
+    } else if (VEC) {
         // 8 consecutive elements per thread per step; slot_numel % 8 == 0 and bases are 16-byte aligned
         for (int64_t e = lo + (int64_t)threadIdx.x * 8; e < hi; e += 256 * 8) {
             const int64_t idx = base + e;
@@ -184,6 +231,7 @@ __device__ __forceinline__ int find_bank(const StreamArgs& p, int64_t blk) {
     return __builtin_amdgcn_readfirstlane(b);
 }
 
+template <bool NT>
 __global__ void __launch_bounds__(256) momentum_kernel(StreamArgs p) {
     const int64_t blk = blockIdx.x;
     const StreamBank& bk = p.bank[find_bank(p, blk)];
@@ -198,11 +246,11 @@ __global__ void __launch_bounds__(256) momentum_kernel(StreamArgs p) {
     __shared__ double red[4];
     double sum;
     if (bk.f32) {
-        sum = bk.vec ? momentum_chunk<true, true>(bk.grad, bk.buf, bk.u, slot, chunk, bk.slot_numel, mu, nu, red)
-                     : momentum_chunk<true, false>(bk.grad, bk.buf, bk.u, slot, chunk, bk.slot_numel, mu, nu, red);
+        sum = bk.vec ? momentum_chunk<true, true, NT>(bk.grad, bk.buf, bk.u, slot, chunk, bk.slot_numel, mu, nu, red)
+                     : momentum_chunk<true, false, NT>(bk.grad, bk.buf, bk.u, slot, chunk, bk.slot_numel, mu, nu, red);
     } else {
-        sum = bk.vec ? momentum_chunk<false, true>(bk.grad, bk.buf, bk.u, slot, chunk, bk.slot_numel, mu, nu, red)
-                     : momentum_chunk<false, false>(bk.grad, bk.buf, bk.u, slot, chunk, bk.slot_numel, mu, nu, red);
+        sum = bk.vec ? momentum_chunk<false, true, NT>(bk.grad, bk.buf, bk.u, slot, chunk, bk.slot_numel, mu, nu, red)
+                     : momentum_chunk<false, false, NT>(bk.grad, bk.buf, bk.u, slot, chunk, bk.slot_numel, mu, nu, red);
     }
     if (threadIdx.x == 0 && bk.partials) bk.partials[slot * bk.nchunks + chunk] = sum;
 }
@@ -315,14 +363,43 @@ __device__ __forceinline__ uint32_t apply_elem(uint32_t hi, uint32_t lo, uint32_
 }
 
 // One chunk of one slot.  VEC: 8 elements per thread per step (slot_numel % 8 == 0, 16-byte aligned bases).
-template <bool VEC>
+template <bool VEC, bool NT>
 __device__ __forceinline__ void apply_chunk(uint16_t* __restrict__ w_hi, uint16_t* __restrict__ w_lo,
                                             const uint16_t* __restrict__ v, int64_t slot, int64_t chunk,
                                             int64_t slot_numel, float eta, float decay) {
     const int64_t base = slot * slot_numel;
     const int64_t lo = chunk * kStreamChunk;
     const int64_t hi = min(lo + kStreamChunk, slot_numel);
-    if (VEC) {
+    if (VEC && NT) {
+        // a stream larger than the last-level cache: every load of the thread's groups before the first
+        // store, all accesses non-temporal, since each element is read and written once (a 2 GB bank: 5.34
+        // TB/s with cached accesses one group at a time, 5.88 TB/s like this)
+        u32x4 h[kStreamGroups], l[kStreamGroups], vv[kStreamGroups];
+#pragma unroll
+        for (int k = 0; k < kStreamGroups; ++k) {
+            const int64_t idx = base + lo + (int64_t)threadIdx.x * 8 + (int64_t)k * 256 * 8;
+            if (idx < base + hi) {
+                h[k] = ld16<NT>(reinterpret_cast<const u32x4*>(w_hi + idx));
+                l[k] = ld16<NT>(reinterpret_cast<const u32x4*>(w_lo + idx));
+                vv[k] = ld16<NT>(reinterpret_cast<const u32x4*>(v + idx));
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kStreamGroups; ++k) {
+            const int64_t idx = base + lo + (int64_t)threadIdx.x * 8 + (int64_t)k * 256 * 8;
+            if (idx >= base + hi) continue;
+            u32x4 ho, lo2;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t r0 = apply_elem(h[k][q] & 0xFFFFu, l[k][q] & 0xFFFFu, vv[k][q] & 0xFFFFu, eta, decay);
+                uint32_t r1 = apply_elem(h[k][q] >> 16, l[k][q] >> 16, vv[k][q] >> 16, eta, decay);
+                ho[q] = (r0 >> 16) | (r1 & 0xFFFF0000u);
+                lo2[q] = (r0 & 0xFFFFu) | (r1 << 16);
+            }
+            st16<NT>(reinterpret_cast<u32x4*>(w_hi + idx), ho);
+            st16<NT>(reinterpret_cast<u32x4*>(w_lo + idx), lo2);
+        }
+    } else if (VEC) {
         for (int64_t e = lo + (int64_t)threadIdx.x * 8; e < hi; e += 256 * 8) {
             const int64_t idx = base + e;
             u32x4 h = *reinterpret_cast<const u32x4*>(w_hi + idx);
@@ -349,6 +426,7 @@ __device__ __forceinline__ void apply_chunk(uint16_t* __restrict__ w_hi, uint16_
     }
 }
 
+template <bool NT>
 __global__ void __launch_bounds__(256) apply_kernel(StreamArgs p) {
     const int64_t blk = blockIdx.x;
     const StreamBank& bk = p.bank[find_bank(p, blk)];
@@ -362,8 +440,8 @@ __global__ void __launch_bounds__(256) apply_kernel(StreamArgs p) {
     } else if (bk.lr_mul_per_slot) {
         eta = __fmul_rn(eta, bk.lr_mul_per_slot[slot]);
     }
-    if (bk.vec) apply_chunk<true>(bk.w_hi, bk.w_lo, bk.v, slot, chunk, bk.slot_numel, eta, decay);
-    else apply_chunk<false>(bk.w_hi, bk.w_lo, bk.v, slot, chunk, bk.slot_numel, eta, decay);
+    if (bk.vec) apply_chunk<true, NT>(bk.w_hi, bk.w_lo, bk.v, slot, chunk, bk.slot_numel, eta, decay);
+    else apply_chunk<false, NT>(bk.w_hi, bk.w_lo, bk.v, slot, chunk, bk.slot_numel, eta, decay);
 }
 
 // ---------------------------------------------------------------------------
@@ -379,24 +457,32 @@ int stream_chunks(int64_t slot_numel) {
 
 namespace {
 
+// Bytes a launch must stream before its accesses go non-temporal (and all its loads first): the 256 MB
+// last-level cache (MALL) of the MI355X.  A smaller stream can stay resident from one step to the next
+// and gains from cached accesses one 8-element group at a time (attention bank, 189 MB of momentum
+// traffic: 4.4 TB/s non-temporal, 4.3 cached with the loads first, 4.7-4.8 cached a group at a time); a
+// larger one is evicted anyway (350M banks: momentum 5.26 -> 5.79 TB/s, apply 5.51 -> 5.80 TB/s).
+constexpr int64_t kNonTemporalBytes = (int64_t)256 << 20;
+
 // Banks [i, i + count) of one launch: their workgroups numbered bank after bank.
 template <class Fill>
-hipError_t launch_streams(int nbanks, const float* slot_scalars, hipStream_t stream, Fill fill,
-                          void (*kernel)(StreamArgs)) {
+hipError_t launch_streams(int nbanks, const float* slot_scalars, hipStream_t stream, Fill fill, int bytes_per_elem,
+                          void (*kernel)(StreamArgs), void (*kernel_nt)(StreamArgs)) {
     for (int i0 = 0; i0 < nbanks; i0 += kMaxStreamBanks) {
         StreamArgs p{};
         p.nbanks = nbanks - i0 < kMaxStreamBanks ? nbanks - i0 : kMaxStreamBanks;
         p.slot_scalars = reinterpret_cast<const f32x4*>(slot_scalars);
-        int64_t blocks = 0;
+        int64_t blocks = 0, bytes = 0;
         for (int j = 0; j < p.nbanks; ++j) {
             StreamBank& b = p.bank[j];
             fill(i0 + j, b);
             b.nchunks = stream_chunks(b.slot_numel);
             b.first_block = blocks;
             blocks += (int64_t)b.batch * b.nchunks;
+            bytes += (int64_t)b.batch * b.slot_numel * bytes_per_elem * (b.f32 ? 2 : 1);
         }
         if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL(bytes >= kNonTemporalBytes ? kernel_nt : kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -419,7 +505,7 @@ hipError_t launch_momentum(const MomentumBank* banks, int nbanks, const float* s
         b.vec = m.slot_numel % 8 == 0 ? 1 : 0;
         b.mu = m.mu;
         b.nu = m.nu;
-    }, momentum_kernel);
+    }, 8, momentum_kernel<false>, momentum_kernel<true>);
 }
 
 hipError_t launch_apply(const ApplyBank* banks, int nbanks, const float* slot_scalars, hipStream_t stream) {
@@ -435,7 +521,7 @@ hipError_t launch_apply(const ApplyBank* banks, int nbanks, const float* slot_sc
         b.vec = a.slot_numel % 8 == 0 ? 1 : 0;
         b.eta = a.eta;
         b.decay = a.decay;
-    }, apply_kernel);
+    }, 10, apply_kernel<false>, apply_kernel<true>);
 }
 
 hipError_t launch_sumsq(const uint16_t* x, double* partials, int64_t batch, int64_t slot_numel, hipStream_t stream) {
