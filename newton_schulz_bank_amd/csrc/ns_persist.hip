@@ -48,18 +48,37 @@ __device__ int g_persist_fault;
 namespace {
 
 constexpr uint64_t kWaitCapTicks = 20000000;   // 200 ms of the 100 MHz constant clock
+// A 256-tile launch takes the three-slot ring from this many bytes of X (all slots of all its banks) on
+constexpr int64_t kAheadMinBytes = (int64_t)128 << 20;
 constexpr int kXccIdReg = 20 | (0 << 6) | (15 << 11);   // hwreg(HW_REG_XCC_ID, 0, 16)
 
 __device__ __forceinline__ int ld_relaxed(const int* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Which operand of each contraction the 256-tile ring copies two stages ahead (false: P, true: Q).
+constexpr bool kQAheadGram = true;
+constexpr bool kQAheadPoly = true;
+constexpr bool kQAheadWideUpdate = true;
+
 template <class C>
 __global__ void __launch_bounds__(C::NT, 2) ns_persist_kernel(PersistArgs p) {
     static_assert(C::BM == C::BN, "square tiles");
     constexpr int kTile = C::BM;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[C::RING];
-    __shared__ int s_task;
+    // The claimed task's index is handed to every wavefront through an LDS word.  The three-slot ring
+    // fills the LDS, so there the word is the ring's last: it belongs to the second slot of the operand
+    // copied one stage ahead, which no copy writes before the first k step of a tile, and every wavefront
+    // reads the index before the barrier ahead of the tile; it lies beyond the epilogue's staging tile.
+    int* task_word;
+    if constexpr (C::PAHEAD) {
+        static_assert(C::RING * 2 - 4 >= C::BM * C::BN * 2, "the task word lies outside the staging tile");
+        task_word = reinterpret_cast<int*>(smem + C::RING) - 1;
+    } else {
+        __shared__ int word;
+        task_word = &word;
+    }
+    int& s_task = *task_word;
     const int tid = threadIdx.x;
     const int q = (int)(__builtin_amdgcn_s_getreg(kXccIdReg) & 0xFFFF) % p.nq;
     const int per_round = p.per_round[q];
@@ -140,8 +159,8 @@ __global__ void __launch_bounds__(C::NT, 2) ns_persist_kernel(PersistArgs p) {
                     const float sc = bk.scale[slot];
                     jb.sig = sc * sc;
                 }
-                if (tall) gemm_tile<false, false, EPI_GRAM, C, POL_SC1>(jb, (lds_u16*)smem, ltid);
-                else gemm_tile<true, true, EPI_GRAM, C, POL_SC1>(jb, (lds_u16*)smem, ltid);
+                if (tall) gemm_tile<false, false, EPI_GRAM, C, POL_SC1, C::PAHEAD && kQAheadGram>(jb, (lds_u16*)smem, ltid);
+                else gemm_tile<true, true, EPI_GRAM, C, POL_SC1, C::PAHEAD && kQAheadGram>(jb, (lds_u16*)smem, ltid);
             }
         } else if (phase == 1) {
             if (live) {
@@ -158,7 +177,7 @@ __global__ void __launch_bounds__(C::NT, 2) ns_persist_kernel(PersistArgs p) {
                 jb.mirror = ti != tj;
                 jb.alpha = p.coef[t][2];
                 jb.beta = p.coef[t][1];
-                gemm_tile<true, true, EPI_POLY, C, POL_SC1>(jb, (lds_u16*)smem, ltid);
+                gemm_tile<true, true, EPI_POLY, C, POL_SC1, C::PAHEAD && kQAheadPoly>(jb, (lds_u16*)smem, ltid);
             }
         } else {
             // wide: X' (m x n) = a*X + B X;  tall: G' (n x m) = a*G + G B
@@ -183,7 +202,7 @@ __global__ void __launch_bounds__(C::NT, 2) ns_persist_kernel(PersistArgs p) {
                 jb.beta = p.coef[t][0];
                 if (t == 0) jb.sig = bk.scale[slot];
                 if (tall) gemm_tile<true, true, EPI_UPDATE, C, POL_SC1>(jb, (lds_u16*)smem, ltid);
-                else gemm_tile<true, false, EPI_UPDATE, C, POL_SC1>(jb, (lds_u16*)smem, ltid);
+                else gemm_tile<true, false, EPI_UPDATE, C, POL_SC1, C::PAHEAD && kQAheadWideUpdate>(jb, (lds_u16*)smem, ltid);
             } else if (last) {
                 // a zero slot's result is exactly zero
                 const int i0 = ti * kTile, j0 = tj * kTile;
@@ -344,8 +363,15 @@ hipError_t ns_persist(const NsPersistBank* banks, int nbanks, int tile, const Ns
     PersistArgs p{};
     fill_persist_args(p, banks, nbanks, tile, coef, steps, d.xccs, sync);
     if (tile == 256) {
-        // one 16-wavefront workgroup per CU (its 128 KiB ring fills the LDS)
-        ns_persist_kernel<Cfg256><<<dim3((unsigned)d.cus), Cfg256::NT, 0, stream>>>(p);
+        // one 16-wavefront workgroup per CU; the three-slot ring (160 KiB) when the launch's X alone is
+        // well beyond what the MALL keeps between a slot's contractions, the two-stage one (128 KiB)
+        // otherwise (350M banks, 708 MB of X: 3 % faster; attention bank, 47 MB: 2 % slower)
+        int64_t xbytes = 0;
+        for (int b = 0; b < nbanks; ++b) xbytes += (int64_t)banks[b].batch * banks[b].rows * banks[b].cols * 2;
+        if (xbytes >= kAheadMinBytes)
+            ns_persist_kernel<Cfg256><<<dim3((unsigned)d.cus), Cfg256::NT, 0, stream>>>(p);
+        else
+            ns_persist_kernel<Cfg256r2><<<dim3((unsigned)d.cus), Cfg256r2::NT, 0, stream>>>(p);
     } else {
         int nmax = 0;
         for (int b = 0; b < nbanks; ++b) nmax = p.bank[b].n > nmax ? p.bank[b].n : nmax;

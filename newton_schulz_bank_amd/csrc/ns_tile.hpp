@@ -9,10 +9,15 @@
 //   POLY   out = alpha*acc + beta*A   symmetric, mirrored
 //   UPDATE out = sig*(acc + beta*X)
 // Operand tiles are copied global -> LDS with MUBUF buffer_load ... lds (16 B
-// per lane) into a two-stage ring, so the copy of stage k+1 overlaps the MFMAs
-// of stage k with no register staging.  (A ring of four 32-k slots, three in
-// flight, measured slower: twice the barriers and half-line row segments cost
-// more than the deeper prefetch gains.)  The LDS layouts are XOR-swizzled so the
+// per lane) into a ring, so the copies of later k stages overlap the MFMAs of
+// stage k with no register staging.  The 128x128 tiles use a two-stage ring
+// (the copy of stage k+1 in flight during stage k).  The 256x256 tiles of
+// launches that stream far more than the MALL holds fill the 160 KiB of LDS
+// with three slots for one operand and two for the other: the first is copied
+// two stages ahead, so its rows that miss the L2 have twice the time to arrive
+// (350M banks: 3 % faster).  (A ring of four 32-k slots, three in flight, measured slower:
+// twice the barriers and half-line row segments cost more than the deeper
+// prefetch gains.)  The LDS layouts are XOR-swizzled so the
 // 16-byte fragment reads and the transposing reads (ds_read_b64_tr_b16) hit
 // distinct banks.  Every global load takes a cache policy: 0, or sc1 so that a
 // load misses the CU's L1 and reads the XCD's L2, which is what a consumer of
@@ -27,17 +32,23 @@ constexpr int kBK = 64;                 // k per ring stage
 enum { EPI_GRAM = 0, EPI_POLY = 1, EPI_UPDATE = 2 };
 enum { POL_DEFAULT = 0, POL_SC1 = 16 }; // cache-policy bits of MUBUF loads (bit 4 = sc1 on gfx940+)
 
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, bool PAHEAD_ = false>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
     static constexpr int NW = WM * WN, NT = 64 * NW;
     static constexpr int TM = BM / WM, TN = BN / WN;      // outputs per wavefront
     static constexpr int FM = TM / 32, FN = TN / 32;      // 32x32 MFMA blocks per wavefront
-    static constexpr int STAGE = (BM + BN) * kBK;         // elements per ring stage (P rows, then Q rows)
-    static constexpr int RING = 2 * STAGE;                // elements of the whole ring
+    // PAHEAD: P slots 0..2 then Q slots 0..1 (P copied two stages ahead); otherwise two stages of
+    // (P rows, then Q rows)
+    static constexpr bool PAHEAD = PAHEAD_;
+    static constexpr int PSLOT = BM * kBK, QSLOT = BN * kBK;             // elements per operand slot
+    static constexpr int NPS = PAHEAD ? 3 : 2;                            // P slots in the ring
+    static constexpr int RING = NPS * PSLOT + 2 * QSLOT;                  // elements of the whole ring
+    static constexpr int NIP = BM / 8 / NW;               // copy instructions per wavefront of a P tile
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tiles are whole MFMA blocks");
     static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "copy instructions split evenly");
     static_assert(BM * BN <= RING, "the epilogue staging tile fits the ring");
+    static_assert(RING * 2 <= 160 * 1024, "the ring fits the LDS");
 };
 using Cfg128 = Cfg<128, 128, 2, 2>;
 // 16 wavefronts of 32x32 on a 128x128 tile: twice the LDS reads per MFMA of 64x64 wave tiles, but a
@@ -47,7 +58,10 @@ using Cfg128w16 = Cfg<128, 128, 4, 4>;
 // 16 wavefronts of 64x64 (four per SIMD, at most 128 VGPRs each): a third more LDS reads per MFMA
 // than 8 wavefronts of 128x64, but four wavefronts per SIMD cover each other's waits, and the
 // epilogue's LDS round trips and stores are spread over twice the wavefronts.
-using Cfg256 = Cfg<256, 256, 4, 4>;
+using Cfg256 = Cfg<256, 256, 4, 4, true>;
+// The same tiles with the two-stage ring: when a launch's operands mostly come from the MALL, copying
+// further ahead only adds requests in flight (attention bank, 40 x 768^2: 2 % slower with three slots).
+using Cfg256r2 = Cfg<256, 256, 4, 4>;
 
 // K-major tile [rows][8 chunks of 8 k]: chunk c of row R sits at entry R*8 + (c ^ ks(R)),
 // conflict-free for the 16 lanes a 16-byte read serves per cycle.
@@ -153,6 +167,11 @@ __device__ __forceinline__ void wait_vmcnt() {
     // s_waitcnt with vmcnt = N (bits 3:0 and 15:14), expcnt and lgkmcnt left at their maxima (no wait)
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+    // vmcnt = N, expcnt = 0, lgkmcnt = 0 (N = 0 is s_waitcnt 0)
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14));
+}
 
 // Upper-triangle tile t (row-major over the triangle of a T x T tile grid) -> (I, J), I <= J.
 __device__ __forceinline__ void sym_tile(int t, int T, int& I, int& J) {
@@ -177,10 +196,14 @@ struct TileJob {
 // tid is the thread's index in the workgroup.  A caller that runs tiles in a loop passes it
 // through an opaque copy made inside the loop, so the per-lane address arithmetic is recomputed
 // per tile instead of being hoisted out of the loop and held in registers across it.
-template <bool P_KMAJOR, bool Q_KMAJOR, int EPI, class C, int POL>
+// QAHEAD (256-tile ring only): Q, not P, takes the three slots and is copied two stages ahead.  The
+// operand to copy ahead is the one whose rows the tiles that run next to each other do not share
+// (for a tile order that walks j fastest, Q), so that more of its first-touch L2 misses have time.
+template <bool P_KMAJOR, bool Q_KMAJOR, int EPI, class C, int POL, bool QAHEAD = false>
 __device__ __forceinline__ void gemm_tile(const TileJob& jb, lds_u16* smem, int tid) {
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // the wavefront's index is uniform: in scalar registers, its row and column offsets cost no VGPRs
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / C::WN, wn = wave % C::WN;
     const int i0 = jb.i0, j0 = jb.j0;
 
@@ -198,10 +221,40 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, lds_u16* smem, int 
     const bool same = P_KMAJOR == Q_KMAJOR && C::BM == C::BN &&
                       __builtin_amdgcn_readfirstlane((int)(i0 == j0 && jb.P[0] == jb.Q[0] && jb.P[1] == jb.Q[1] &&
                                                            jb.ldp == jb.ldq)) != 0;
-    const int qoff = same ? 0 : C::BM * kBK;            // Q's offset in a ring stage (elements)
-    load_tile_lds<P_KMAJOR, C::BM, C::NW, POL>(jb.P, jb.ldp, i0, 0, smem, wave, lane);
-    if (!same) load_tile_lds<Q_KMAJOR, C::BN, C::NW, POL>(jb.Q, jb.ldq, j0, 0, smem + C::BM * kBK, wave, lane);
-    wait_vmcnt<0>();
+    // The ring: NPS slots of the operand copied ahead (P, or Q with QAHEAD; a diagonal tile copies
+    // only P and always ahead), then two slots of the other.  Stage kt's operands sit in slot kt % NPS
+    // of the first group and slot kt % 2 of the second.
+    static_assert(!QAHEAD || (C::PAHEAD && C::BM == C::BN), "Q ahead needs the three-slot ring of square tiles");
+    const bool qa = QAHEAD && !same;
+    auto slot3 = [&](int s) { return smem + s * C::PSLOT; };
+    auto slot2 = [&](int s) { return smem + C::NPS * C::PSLOT + s * C::QSLOT; };
+    auto pslot = [&](int s3, int s2) { return qa ? slot2(s2) : slot3(s3); };
+    auto qslot = [&](int s3, int s2) { return same ? slot3(s3) : (qa ? slot3(s3) : slot2(s2)); };
+    auto copy_p = [&](int kt, lds_u16* dst) {
+        load_tile_lds<P_KMAJOR, C::BM, C::NW, POL>(jb.P, jb.ldp, i0, kt * kBK, dst, wave, lane);
+    };
+    auto copy_q = [&](int kt, lds_u16* dst) {
+        if (!same) load_tile_lds<Q_KMAJOR, C::BN, C::NW, POL>(jb.Q, jb.ldq, j0, kt * kBK, dst, wave, lane);
+    };
+    // copies of one stage's operand ahead of the other's, and of the other's (the ahead operand's
+    // instruction count is what a wait that leaves it in flight allows)
+    auto copy_ahead = [&](int kt, int s3) {
+        if (qa) copy_q(kt, slot3(s3));
+        else copy_p(kt, slot3(s3));
+    };
+    auto copy_other = [&](int kt, int s2) {
+        if (qa) copy_p(kt, slot2(s2));
+        else copy_q(kt, slot2(s2));
+    };
+    copy_ahead(0, 0);
+    copy_other(0, 0);
+    if (C::PAHEAD && KT > 1) {
+        // the ahead operand of stage 1 stays in flight: the wait below covers everything issued before it
+        copy_ahead(1, 1);
+        wait_vmcnt<C::NIP>();
+    } else {
+        wait_vmcnt<0>();
+    }
     __builtin_amdgcn_s_barrier();
 
     // fragments double-buffered in registers: the reads of step kk+1 are issued before
@@ -209,21 +262,28 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, lds_u16* smem, int 
     // ahead of the last MFMAs of the current one
     bf16x8 pf[2][C::FM], qf[2][C::FN];
 #pragma unroll
-    for (int a = 0; a < C::FM; ++a) pf[0][a] = read_frag_fast<P_KMAJOR, C::BM>(smem, wm * C::TM + a * 32, 0, lane);
+    for (int a = 0; a < C::FM; ++a)
+        pf[0][a] = read_frag_fast<P_KMAJOR, C::BM>(pslot(0, 0), wm * C::TM + a * 32, 0, lane);
 #pragma unroll
     for (int b = 0; b < C::FN; ++b)
-        qf[0][b] = read_frag_fast<Q_KMAJOR, C::BN>(smem + qoff, wn * C::TN + b * 32, 0, lane);
+        qf[0][b] = read_frag_fast<Q_KMAJOR, C::BN>(qslot(0, 0), wn * C::TN + b * 32, 0, lane);
 
+    int s3 = 0;                                          // kt % NPS
     for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        const lds_u16* lp = smem + cur * C::STAGE;
+        const int s2 = kt & 1;
+        const int n3 = s3 + 1 == C::NPS ? 0 : s3 + 1;    // (kt + 1) % NPS
+        const lds_u16* lp = pslot(s3, s2);
+        const lds_u16* lq = qslot(s3, s2);
         const bool more = kt + 1 < KT;
-        if (more) {
-            lds_u16* np = smem + (cur ^ 1) * C::STAGE;
-            load_tile_lds<P_KMAJOR, C::BM, C::NW, POL>(jb.P, jb.ldp, i0, (kt + 1) * kBK, np, wave, lane);
-            if (!same)
-                load_tile_lds<Q_KMAJOR, C::BN, C::NW, POL>(jb.Q, jb.ldq, j0, (kt + 1) * kBK, np + C::BM * kBK, wave,
-                                                           lane);
+        // the slots of stage kt - 1 are free (every wave passed the barrier after reading them)
+        bool ahead = false;
+        if (C::PAHEAD) {
+            if (more) copy_other(kt + 1, s2 ^ 1);
+            ahead = kt + 2 < KT;
+            if (ahead) copy_ahead(kt + 2, n3 + 1 == C::NPS ? 0 : n3 + 1);
+        } else if (more) {
+            copy_ahead(kt + 1, n3);
+            copy_other(kt + 1, s2 ^ 1);
         }
 #pragma unroll
         for (int kk = 0; kk < kBK / 16; ++kk) {
@@ -234,18 +294,22 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, lds_u16* smem, int 
                     pf[nb][a] = read_frag_fast<P_KMAJOR, C::BM>(lp, wm * C::TM + a * 32, kk + 1, lane);
 #pragma unroll
                 for (int b = 0; b < C::FN; ++b)
-                    qf[nb][b] = read_frag_fast<Q_KMAJOR, C::BN>(lp + qoff, wn * C::TN + b * 32, kk + 1, lane);
+                    qf[nb][b] = read_frag_fast<Q_KMAJOR, C::BN>(lq, wn * C::TN + b * 32, kk + 1, lane);
             } else if (more) {
-                // every wave's reads of this stage are done and the next stage has landed
-                __builtin_amdgcn_s_waitcnt(0);
+                // every wave's reads of this stage are done and the next stage has landed (with the
+                // three-slot ring, the copy of stage kt + 2's ahead operand, issued last, may still be
+                // in flight)
+                if (ahead) wait_vmcnt_lgkm0<C::NIP>();
+                else wait_vmcnt_lgkm0<0>();
                 __builtin_amdgcn_s_barrier();
-                const lds_u16* np = smem + (cur ^ 1) * C::STAGE;
+                const lds_u16* np = pslot(n3, s2 ^ 1);
+                const lds_u16* nq = qslot(n3, s2 ^ 1);
 #pragma unroll
                 for (int a = 0; a < C::FM; ++a)
                     pf[nb][a] = read_frag_fast<P_KMAJOR, C::BM>(np, wm * C::TM + a * 32, 0, lane);
 #pragma unroll
                 for (int b = 0; b < C::FN; ++b)
-                    qf[nb][b] = read_frag_fast<Q_KMAJOR, C::BN>(np + qoff, wn * C::TN + b * 32, 0, lane);
+                    qf[nb][b] = read_frag_fast<Q_KMAJOR, C::BN>(nq, wn * C::TN + b * 32, 0, lane);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -255,6 +319,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, lds_u16* smem, int 
                     acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[fb][b], pf[fb][a], acc[a][b], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
+        s3 = n3;
     }
 
     // ---- epilogue, staged through LDS so that every global access is a full coalesced row:
