@@ -38,13 +38,15 @@ struct Cfg {
     static constexpr int NW = WM * WN, NT = 64 * NW;
     static constexpr int TM = BM / WM, TN = BN / WN;      // outputs per wavefront
     static constexpr int FM = TM / 32, FN = TN / 32;      // 32x32 MFMA blocks per wavefront
-    // PAHEAD: P slots 0..2 then Q slots 0..1 (P copied two stages ahead); otherwise two stages of
-    // (P rows, then Q rows)
+    // PAHEAD: three slots for the operand copied two stages ahead (P, or Q when the tile asks for it),
+    // then two for the other; otherwise two slots for each (P's first)
     static constexpr bool PAHEAD = PAHEAD_;
     static constexpr int PSLOT = BM * kBK, QSLOT = BN * kBK;             // elements per operand slot
-    static constexpr int NPS = PAHEAD ? 3 : 2;                            // P slots in the ring
+    static constexpr int NPS = PAHEAD ? 3 : 2;                            // slots of the first group
     static constexpr int RING = NPS * PSLOT + 2 * QSLOT;                  // elements of the whole ring
-    static constexpr int NIP = BM / 8 / NW;               // copy instructions per wavefront of a P tile
+    // copy instructions per wavefront of one operand tile (P's; Q's too when the tile is square, which
+    // copying Q ahead requires)
+    static constexpr int NIP = BM / 8 / NW;
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tiles are whole MFMA blocks");
     static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "copy instructions split evenly");
     static_assert(BM * BN <= RING, "the epilogue staging tile fits the ring");
