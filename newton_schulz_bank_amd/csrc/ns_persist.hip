@@ -213,17 +213,17 @@ __global__ void __launch_bounds__(C::NT, 2) ns_persist_kernel(PersistArgs p) {
             }
         }
 
-        // publish: every store of this workgroup is in the L2 before the counter moves; then
-        // claim the next task (claiming earlier, while a tile is still running, holds back
-        // tasks that another workgroup could start at once)
+        // claim the next task while this one's stores drain (the claim's round trip and the stores'
+        // acknowledgements overlap; claiming earlier, while a tile is still running, would hold back
+        // tasks that another workgroup could start at once), then publish: every store of this
+        // workgroup is in the L2 before the counter moves.  The next task may wait for this one:
+        // this workgroup moves the counter before it checks the next task's dependency.
+        int got = 0;
+        if (leader) got = __hip_atomic_fetch_add(p.heads + q, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (leader) s_task = __builtin_amdgcn_readfirstlane(got);
         __syncthreads();
-        if (leader) {
-            __hip_atomic_fetch_add(ctr, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            s_task = __builtin_amdgcn_readfirstlane(
-                __hip_atomic_fetch_add(p.heads + q, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        }
-        __syncthreads();
+        if (leader) __hip_atomic_fetch_add(ctr, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         idx = __builtin_amdgcn_readfirstlane(s_task);
     }
 
