@@ -50,6 +50,8 @@ namespace {
 constexpr uint64_t kWaitCapTicks = 20000000;   // 200 ms of the 100 MHz constant clock
 // A 256-tile launch takes the three-slot ring from this many bytes of X (all slots of all its banks) on
 constexpr int64_t kAheadMinBytes = (int64_t)128 << 20;
+// Tasks of one round per queue, in units of the queue's workgroups, from which a launch claims early
+constexpr int kEarlyClaimDepth = 2;
 constexpr int kXccIdReg = 20 | (0 << 6) | (15 << 11);   // hwreg(HW_REG_XCC_ID, 0, 16)
 
 __device__ __forceinline__ int ld_relaxed(const int* p) {
@@ -213,17 +215,31 @@ __global__ void __launch_bounds__(C::NT, 2) ns_persist_kernel(PersistArgs p) {
             }
         }
 
-        // claim the next task while this one's stores drain (the claim's round trip and the stores'
-        // acknowledgements overlap; claiming earlier, while a tile is still running, would hold back
-        // tasks that another workgroup could start at once), then publish: every store of this
-        // workgroup is in the L2 before the counter moves.  The next task may wait for this one:
-        // this workgroup moves the counter before it checks the next task's dependency.
-        int got = 0;
-        if (leader) got = __hip_atomic_fetch_add(p.heads + q, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        if (leader) s_task = __builtin_amdgcn_readfirstlane(got);
-        __syncthreads();
-        if (leader) __hip_atomic_fetch_add(ctr, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // publish: every store of this workgroup is in the L2 before the counter moves; and claim
+        // the next task.  With claim_early the claim goes out while this tile's stores drain, so
+        // its round trip and their acknowledgements overlap (and one barrier goes); the next task
+        // may wait for this one, and this workgroup moves the counter before it checks the next
+        // task's dependency.  Claiming early holds a task back for the length of the drain, which
+        // costs a launch whose queues are short (idle workgroups could have started it at once),
+        // so those claim after the drain.
+        if (p.claim_early) {
+            int got = 0;
+            if (leader)
+                got = __hip_atomic_fetch_add(p.heads + q, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            if (leader) s_task = __builtin_amdgcn_readfirstlane(got);
+            __syncthreads();
+            if (leader) __hip_atomic_fetch_add(ctr, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (leader) {
+                __hip_atomic_fetch_add(ctr, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                s_task = __builtin_amdgcn_readfirstlane(
+                    __hip_atomic_fetch_add(p.heads + q, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            }
+            __syncthreads();
+        }
         idx = __builtin_amdgcn_readfirstlane(s_task);
     }
 
@@ -352,6 +368,14 @@ int ns_persist_tile(int64_t rows, int64_t cols, int steps, int64_t slots) {
     return 0;
 }
 
+// A 128-tile launch whose slots' long side is at most 768 runs one 16-wavefront workgroup per CU (its tasks
+// are short); longer ones two 4-wavefront workgroups per CU.
+static bool short128(const PersistArgs& p) {
+    int nmax = 0;
+    for (int b = 0; b < p.nbanks; ++b) nmax = p.bank[b].n > nmax ? p.bank[b].n : nmax;
+    return nmax <= 768;
+}
+
 hipError_t ns_persist(const NsPersistBank* banks, int nbanks, int tile, const NsCoef* coef, int steps, int* sync,
                       hipStream_t stream) {
     if (nbanks < 1 || nbanks > kMaxPersistBanks || (tile != 256 && tile != 128) || steps < 1 || steps > kMaxRounds)
@@ -362,6 +386,12 @@ hipError_t ns_persist(const NsPersistBank* banks, int nbanks, int tile, const Ns
     if (!d.understood) return hipErrorNotSupported;
     PersistArgs p{};
     fill_persist_args(p, banks, nbanks, tile, coef, steps, d.xccs, sync);
+    // claim early only when every queue holds at least kEarlyClaimDepth rounds of tasks for its
+    // workgroups (350M banks: -4.5 %; four 256^2 slots, one per XCD: +24 % when claiming early)
+    const int wg_per_queue = (tile == 128 && !short128(p) ? 2 : 1) * d.cus / d.xccs;
+    int min_round = 1 << 30;
+    for (int qq = 0; qq < p.nq; ++qq) min_round = p.per_round[qq] < min_round ? p.per_round[qq] : min_round;
+    p.claim_early = min_round >= kEarlyClaimDepth * wg_per_queue ? 1 : 0;
     if (tile == 256) {
         // one 16-wavefront workgroup per CU; the three-slot ring (160 KiB) when the launch's X alone is
         // well beyond what the MALL keeps between a slot's contractions, the two-stage one (128 KiB)
@@ -373,9 +403,7 @@ hipError_t ns_persist(const NsPersistBank* banks, int nbanks, int tile, const Ns
         else
             ns_persist_kernel<Cfg256r2><<<dim3((unsigned)d.cus), Cfg256r2::NT, 0, stream>>>(p);
     } else {
-        int nmax = 0;
-        for (int b = 0; b < nbanks; ++b) nmax = p.bank[b].n > nmax ? p.bank[b].n : nmax;
-        if (nmax <= 768) {
+        if (short128(p)) {
             // short contractions: one 16-wavefront workgroup per CU finishes each task sooner (four
             // 256^2 slots -16 %, six 384^2 -20 %, five 768^2 -2 %; all bit-identical)
             ns_persist_kernel<Cfg128w16><<<dim3((unsigned)d.cus), Cfg128w16::NT, 0, stream>>>(p);

@@ -48,6 +48,7 @@ struct PersistArgs {
     int per_round[kMaxQueues], blk_g[kMaxQueues], blk_p[kMaxQueues];
     int ls[kMaxQueues][kMaxPersistBanks];
     float coef[kMaxRounds][3];   // (a, b, c) of each round
+    int claim_early;        // claim the next task while a finished tile's stores drain (set at launch)
 };
 
 __host__ __device__ __forceinline__ int sym_count(int tm) { return tm * (tm + 1) / 2; }
