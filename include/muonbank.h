@@ -119,18 +119,26 @@ const char *mb_version(void);
 mb_status mb_slot_scalars_fill(const mb_bank *banks, int32_t num_banks, const mb_hparams *hp,
                                float *host_table, int64_t capacity);
 
-/* What muon_bank_step would enqueue for these banks on a device with num_xcds XCDs (MI355X: 8), under
- * the current mb_ns_set_path setting: kernel launches by kind (total excludes the device-to-device
- * copies of one-round calls), and the tile edge of each persistent launch.  Every persistent launch's
- * task lists are checked on the host with the kernel's own decode: each task of each slot listed
- * exactly once, on its slot's queue, after every task it waits for (MB_ERR_VALUE with the reason if
- * not).  Host only; touches no device. */
+/* What muon_bank_step would enqueue for these banks on a device of num_cus compute units in num_xcds
+ * XCDs (MI355X: 256 and 8), under the current mb_ns_set_path setting: kernel launches by kind (total
+ * excludes the device-to-device copies of one-round calls) and, for each persistent launch (the first
+ * 8), its tile edge, its ring (3: the 256-tile ring that copies one operand two stages ahead, taken
+ * when the launch's X is at least 128 MiB; 2: the two-stage ring), its workgroups, and whether they
+ * claim their next task while a finished tile's stores drain (when every XCD queue holds at least two
+ * rounds of tasks per workgroup).  Every persistent launch's task lists are checked on the host with
+ * the kernel's own decode: each task of each slot listed exactly once, on its slot's queue, after
+ * every task it waits for (MB_ERR_VALUE with the reason if not).  A device whose CU count is not a
+ * multiple of its XCD count (or with more than 16 XCDs) gets no persistent launch.  Host only;
+ * touches no device. */
 typedef struct {
     int32_t momentum, ns_scale, ns_persist, ns_small, ns_per_contraction, apply, copies, total;
     int32_t persist_tile[8];
+    int32_t persist_ring[8];
+    int32_t persist_workgroups[8];
+    int32_t persist_claim_early[8];
 } mb_step_plan_info;
-mb_status mb_step_plan(const mb_bank *banks, int32_t num_banks, const mb_hparams *hp, int32_t num_xcds,
-                       mb_step_plan_info *out);
+mb_status mb_step_plan(const mb_bank *banks, int32_t num_banks, const mb_hparams *hp, int32_t num_cus,
+                       int32_t num_xcds, mb_step_plan_info *out);
 
 /* Workspace bytes needed by muon_bank_step for these banks (0 on invalid shapes). */
 size_t mb_step_workspace_bytes(const mb_bank *banks, int32_t num_banks);

@@ -54,7 +54,9 @@ class mb_bank(ctypes.Structure):
 
 class mb_step_plan_info(ctypes.Structure):
     _fields_ = [(k, ctypes.c_int32) for k in ("momentum", "ns_scale", "ns_persist", "ns_small", "ns_per_contraction",
-                                              "apply", "copies", "total")] + [("persist_tile", ctypes.c_int32 * 8)]
+                                              "apply", "copies", "total")] + \
+               [(k, ctypes.c_int32 * 8) for k in ("persist_tile", "persist_ring", "persist_workgroups",
+                                                  "persist_claim_early")]
 
 
 class mb_kernel_time(ctypes.Structure):
@@ -86,7 +88,7 @@ def lib() -> ctypes.CDLL:
         "mb_version": (ctypes.c_char_p, []),
         "mb_step_workspace_bytes": (sz, [ctypes.POINTER(mb_bank), i32]),
         "mb_slot_scalars_fill": (i32, [ctypes.POINTER(mb_bank), i32, ctypes.POINTER(mb_hparams), vp, i64]),
-        "mb_step_plan": (i32, [ctypes.POINTER(mb_bank), i32, ctypes.POINTER(mb_hparams), i32,
+        "mb_step_plan": (i32, [ctypes.POINTER(mb_bank), i32, ctypes.POINTER(mb_hparams), i32, i32,
                                ctypes.POINTER(mb_step_plan_info)]),
         "mb_ns_workspace_bytes": (sz, [i64, i64, i64]),
         "muon_bank_step": (i32, [ctypes.POINTER(mb_bank), i32, ctypes.POINTER(mb_hparams), vp, sz, vp]),

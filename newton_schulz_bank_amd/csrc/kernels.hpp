@@ -128,6 +128,14 @@ bool ns_persist_supported();
 bool ns_persist_fits256(int64_t rows, int64_t cols);
 hipError_t ns_persist(const NsPersistBank* banks, int nbanks, int tile, const NsCoef* coef, int steps, int* sync,
                       hipStream_t stream);
+// How a persistent launch runs on a device of `cus` compute units in `xccs` XCDs: the ring of its
+// tiles (slots of the operand copied ahead: 3 for the 256-tiles of launches whose X is at least
+// 128 MiB, else 2), its workgroups per XCD queue, its wavefronts per workgroup, and whether its
+// workgroups claim their next task while a finished tile's stores drain.
+struct PersistLaunch {
+    int ring, wg_per_queue, wavefronts, claim_early;
+};
+PersistLaunch ns_persist_launch(const NsPersistBank* banks, int nbanks, int tile, int steps, int cus, int xccs);
 // Host check of one persistent launch's task lists with nq queues, by the kernel's own decode: every
 // task of every slot's chains listed exactly once, on its slot's queue, each after every task it waits
 // for.  On failure returns false with a reason in why.

@@ -371,8 +371,8 @@ mb_status mb_slot_scalars_fill(const mb_bank* banks, int32_t num_banks, const mb
     return ok();
 }
 
-mb_status mb_step_plan(const mb_bank* banks, int32_t num_banks, const mb_hparams* hp_in, int32_t num_xcds,
-                       mb_step_plan_info* out) {
+mb_status mb_step_plan(const mb_bank* banks, int32_t num_banks, const mb_hparams* hp_in, int32_t num_cus,
+                       int32_t num_xcds, mb_step_plan_info* out) {
     if (!banks || !out) return fail(MB_ERR_NULL, "mb_step_plan: null pointer");
     if (num_banks <= 0 || num_banks > 1024) return fail(MB_ERR_SHAPE, "mb_step_plan: num_banks must be in 1..1024");
     mb_hparams hp;
@@ -387,7 +387,8 @@ mb_status mb_step_plan(const mb_bank* banks, int32_t num_banks, const mb_hparams
     mb_step_plan_info info{};
     const int groups = (num_banks + mb::kMaxStreamBanks - 1) / mb::kMaxStreamBanks;
     info.momentum = info.ns_scale = info.apply = groups;
-    const bool persist = g_ns_path.load() == 0 && num_xcds >= 1 && num_xcds <= 16;
+    const bool persist = g_ns_path.load() == 0 && num_xcds >= 1 && num_xcds <= 16 && num_cus >= num_xcds &&
+                         num_cus % num_xcds == 0;
     const StepPlan plan = plan_step(banks, num_banks);
     int small = 0;
     for (int32_t i = 0; i < num_banks; ++i) {
@@ -408,8 +409,15 @@ mb_status mb_step_plan(const mb_bank* banks, int32_t num_banks, const mb_hparams
             if (!mb::ns_persist_check(pb.data(), (int)pb.size(), c.tile, hp.ns_steps, num_xcds, why, sizeof why))
                 return fail(MB_ERR_VALUE, "mb_step_plan: persistent launch of %zu banks, %d-tiles: %s", c.banks.size(),
                             c.tile, why);
+            const mb::PersistLaunch l = mb::ns_persist_launch(pb.data(), (int)pb.size(), c.tile, hp.ns_steps, num_cus,
+                                                              num_xcds);
+            if (info.ns_persist < 8) {
+                info.persist_tile[info.ns_persist] = c.tile;
+                info.persist_ring[info.ns_persist] = l.ring;
+                info.persist_workgroups[info.ns_persist] = l.wg_per_queue * num_xcds;
+                info.persist_claim_early[info.ns_persist] = l.claim_early;
+            }
             ++info.ns_persist;
-            info.persist_tile[info.ns_persist - 1 < 8 ? info.ns_persist - 1 : 7] = c.tile;
         }
     }
     info.total = info.momentum + info.ns_scale + info.ns_persist + info.ns_small + info.ns_per_contraction + info.apply;

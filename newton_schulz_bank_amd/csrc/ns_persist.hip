@@ -376,6 +376,45 @@ static bool short128(const PersistArgs& p) {
     return nmax <= 768;
 }
 
+static PersistLaunch launch_of(const PersistArgs& p, const NsPersistBank* banks, int nbanks, int tile, int cus,
+                               int xccs) {
+    PersistLaunch l{};
+    if (tile == 256) {
+        // one 16-wavefront workgroup per CU; the three-slot ring (160 KiB) when the launch's X alone is
+        // well beyond what the MALL keeps between a slot's contractions, the two-stage one (128 KiB)
+        // otherwise (350M banks, 708 MB of X: 3 % faster; attention bank, 47 MB: 2 % slower)
+        int64_t xbytes = 0;
+        for (int b = 0; b < nbanks; ++b) xbytes += (int64_t)banks[b].batch * banks[b].rows * banks[b].cols * 2;
+        l.ring = xbytes >= kAheadMinBytes ? 3 : 2;
+        l.wavefronts = Cfg256::NW;
+        l.wg_per_queue = cus / xccs;
+    } else if (short128(p)) {
+        // short contractions: one 16-wavefront workgroup per CU finishes each task sooner (four 256^2
+        // slots -16 %, six 384^2 -20 %, five 768^2 -2 %; all bit-identical)
+        l.ring = 2;
+        l.wavefronts = Cfg128w16::NW;
+        l.wg_per_queue = cus / xccs;
+    } else {
+        // two 4-wavefront workgroups per CU (three 3072 x 768 slots: 9 % faster than 16 wavefronts, eight
+        // 1024^2: 15 %)
+        l.ring = 2;
+        l.wavefronts = Cfg128::NW;
+        l.wg_per_queue = 2 * cus / xccs;
+    }
+    // claim early only when every queue holds at least kEarlyClaimDepth rounds of tasks for its
+    // workgroups (350M banks: -4.5 %; four 256^2 slots, one per XCD: +24 % when claiming early)
+    int min_round = 1 << 30;
+    for (int q = 0; q < p.nq; ++q) min_round = p.per_round[q] < min_round ? p.per_round[q] : min_round;
+    l.claim_early = min_round >= kEarlyClaimDepth * l.wg_per_queue ? 1 : 0;
+    return l;
+}
+
+PersistLaunch ns_persist_launch(const NsPersistBank* banks, int nbanks, int tile, int steps, int cus, int xccs) {
+    PersistArgs p{};
+    fill_persist_args(p, banks, nbanks, tile, nullptr, steps, xccs, nullptr);
+    return launch_of(p, banks, nbanks, tile, cus, xccs);
+}
+
 hipError_t ns_persist(const NsPersistBank* banks, int nbanks, int tile, const NsCoef* coef, int steps, int* sync,
                       hipStream_t stream) {
     if (nbanks < 1 || nbanks > kMaxPersistBanks || (tile != 256 && tile != 128) || steps < 1 || steps > kMaxRounds)
@@ -386,33 +425,17 @@ hipError_t ns_persist(const NsPersistBank* banks, int nbanks, int tile, const Ns
     if (!d.understood) return hipErrorNotSupported;
     PersistArgs p{};
     fill_persist_args(p, banks, nbanks, tile, coef, steps, d.xccs, sync);
-    // claim early only when every queue holds at least kEarlyClaimDepth rounds of tasks for its
-    // workgroups (350M banks: -4.5 %; four 256^2 slots, one per XCD: +24 % when claiming early)
-    const int wg_per_queue = (tile == 128 && !short128(p) ? 2 : 1) * d.cus / d.xccs;
-    int min_round = 1 << 30;
-    for (int qq = 0; qq < p.nq; ++qq) min_round = p.per_round[qq] < min_round ? p.per_round[qq] : min_round;
-    p.claim_early = min_round >= kEarlyClaimDepth * wg_per_queue ? 1 : 0;
-    if (tile == 256) {
-        // one 16-wavefront workgroup per CU; the three-slot ring (160 KiB) when the launch's X alone is
-        // well beyond what the MALL keeps between a slot's contractions, the two-stage one (128 KiB)
-        // otherwise (350M banks, 708 MB of X: 3 % faster; attention bank, 47 MB: 2 % slower)
-        int64_t xbytes = 0;
-        for (int b = 0; b < nbanks; ++b) xbytes += (int64_t)banks[b].batch * banks[b].rows * banks[b].cols * 2;
-        if (xbytes >= kAheadMinBytes)
-            ns_persist_kernel<Cfg256><<<dim3((unsigned)d.cus), Cfg256::NT, 0, stream>>>(p);
-        else
-            ns_persist_kernel<Cfg256r2><<<dim3((unsigned)d.cus), Cfg256r2::NT, 0, stream>>>(p);
-    } else {
-        if (short128(p)) {
-            // short contractions: one 16-wavefront workgroup per CU finishes each task sooner (four
-            // 256^2 slots -16 %, six 384^2 -20 %, five 768^2 -2 %; all bit-identical)
-            ns_persist_kernel<Cfg128w16><<<dim3((unsigned)d.cus), Cfg128w16::NT, 0, stream>>>(p);
-        } else {
-            // two 4-wavefront workgroups per CU (three 3072 x 768 slots: 9 % faster than 16 wavefronts,
-            // eight 1024^2: 15 %)
-            ns_persist_kernel<Cfg128><<<dim3((unsigned)(2 * d.cus)), Cfg128::NT, 0, stream>>>(p);
-        }
-    }
+    const PersistLaunch l = launch_of(p, banks, nbanks, tile, d.cus, d.xccs);
+    p.claim_early = l.claim_early;
+    const dim3 grid((unsigned)(l.wg_per_queue * d.xccs));
+    if (tile == 256 && l.ring == 3)
+        ns_persist_kernel<Cfg256><<<grid, Cfg256::NT, 0, stream>>>(p);
+    else if (tile == 256)
+        ns_persist_kernel<Cfg256r2><<<grid, Cfg256r2::NT, 0, stream>>>(p);
+    else if (l.wavefronts == Cfg128w16::NW)
+        ns_persist_kernel<Cfg128w16><<<grid, Cfg128w16::NT, 0, stream>>>(p);
+    else
+        ns_persist_kernel<Cfg128><<<grid, Cfg128::NT, 0, stream>>>(p);
     return hipGetLastError();
 }
 

@@ -32,10 +32,11 @@ def _banks(shapes):
     return (api.mb_bank * len(out))(*out), len(out)
 
 
-def plan(L, shapes, xcds=8, hp=None):
+def plan(L, shapes, xcds=8, hp=None, cus=None):
     arr, n = _banks(shapes)
     info = api.mb_step_plan_info()
-    st = L.mb_step_plan(arr, n, ctypes.byref(hp) if hp is not None else None, xcds, ctypes.byref(info))
+    cus = 32 * xcds if cus is None else cus
+    st = L.mb_step_plan(arr, n, ctypes.byref(hp) if hp is not None else None, cus, xcds, ctypes.byref(info))
     assert st == 0, L.mb_last_error().decode()
     return info
 
@@ -101,3 +102,33 @@ def test_more_banks_than_one_launch_holds(L):
     info = plan(L, [(3, 256, 512)] * 20)
     assert info.momentum == 2 and info.apply == 2 and info.ns_scale == 2
     assert info.ns_persist == 3
+
+
+# (tile, ring, workgroups, claim_early) of each workload's persistent launch on 256 CUs in 8 XCDs: the
+# three-slot ring from 128 MiB of X (the 124M step's two big banks: 160 MB; the 350M banks: 708 MB), early
+# claims where every queue holds two rounds of tasks per workgroup (not one slot per XCD: workloads 0, 5)
+LAUNCHES = {0: (128, 2, 256, 0), 1: (256, 2, 256, 1), 2: (256, 2, 256, 1), 3: (256, 3, 256, 1),
+            4: (256, 3, 256, 1), 5: (128, 2, 512, 0), 6: (256, 2, 256, 1), 7: (256, 3, 256, 1)}
+
+
+@pytest.mark.parametrize("config", sorted(LAUNCHES))
+def test_persistent_launch_choices(L, config):
+    info = plan(L, shapes_of(config), 8, cus=256)
+    assert info.ns_persist == 1
+    got = (info.persist_tile[0], info.persist_ring[0], info.persist_workgroups[0], info.persist_claim_early[0])
+    assert got == LAUNCHES[config], (config, got)
+
+
+def test_ring_threshold_is_128_mib_of_x(L):
+    """40 attention slots (47 MB of X) keep the two-stage ring; 112 of them (132 MB) too; 114 (134.5 MB) take
+    the three-slot ring."""
+    for batch, ring in ((40, 2), (112, 2), (114, 3)):
+        info = plan(L, [(batch, 768, 768)], 8, cus=256)
+        assert info.persist_ring[0] == ring, (batch, info.persist_ring[0])
+
+
+def test_a_device_layout_the_launch_does_not_take(L):
+    """With a CU count that is not a multiple of the XCD count the step plans no persistent launch: every
+    contraction is its own launch."""
+    info = plan(L, shapes_of(1), 8, cus=250)
+    assert info.ns_persist == 0 and info.ns_per_contraction == 15
