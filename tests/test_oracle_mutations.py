@@ -1,0 +1,109 @@
+"""Planted mistakes in the oracle, each caught by a pin (CPU only).
+
+Every case edits one line of the oracle's source (a dropped term, a transposed operand, a wrong norm, a
+missing round, swapped coefficients, a rounding where the pages slice bits, ...), executes the edited
+functions in a copy of the oracle's namespace, binds them where a pin test looks them up, and runs that
+pin: it must fail.  The unedited oracle passes the same pins in tests/test_oracle_*.py.  A case whose
+source line is no longer in the oracle fails too, so an edit of the oracle cannot silently retire a case.
+
+One plausible mistake is not on the list because no pin can catch it: working on a tall slot without
+transposing it gives the same result in exact arithmetic (p(X^T) = p(X)^T), only with the larger Gram.
+"""
+
+import inspect
+
+import pytest
+
+import oracle.muon as om
+from tests import test_oracle_apply, test_oracle_momentum, test_oracle_ns, test_oracle_rounding, test_oracle_step
+
+
+def mutant(edits, rebuild):
+    """Namespace copy of oracle.muon in which `edits` [(function, old line text, new text)] are applied
+    and every function in `rebuild` is re-executed, so that they call the edited ones."""
+    ns = dict(om.__dict__)
+    names = list(dict.fromkeys([e[0] for e in edits] + list(rebuild)))
+    for name in names:
+        src = inspect.getsource(getattr(om, name))
+        for fn, old, new in edits:
+            if fn == name:
+                assert old in src, f"{name}: the line to edit is gone from the oracle: {old!r}"
+                src = src.replace(old, new)
+        exec(compile(src, f"<mutant {name}>", "exec"), ns)
+    return ns
+
+
+# (case id, edits, functions to re-execute, {pin module: names to rebind}, pin test, its arguments)
+CASES = [
+    ("ns drops the c*A*A term",
+     [("newton_schulz", "poly = rb * gram + rc * (gram @ gram)", "poly = rb * gram")], [],
+     {test_oracle_ns: ["newton_schulz"]}, test_oracle_ns.test_ns_equals_svd_closed_form, ((8, 8),)),
+    ("ns Gram of the transpose",
+     [("newton_schulz", "gram = x @ x.T", "gram = x.T @ x")], [],
+     {test_oracle_ns: ["newton_schulz"]}, test_oracle_ns.test_ns_equals_svd_closed_form, ((8, 8),)),
+    ("ns update subtracts B X",
+     [("newton_schulz", "x = ra * x + poly @ x", "x = ra * x - poly @ x")], [],
+     {test_oracle_ns: ["newton_schulz"]}, test_oracle_ns.test_ns_equals_svd_closed_form, ((4, 16),)),
+    ("ns one round short",
+     [("newton_schulz", "for (ra, rb, rc) in schedule:", "for (ra, rb, rc) in schedule[:-1]:")], [],
+     {test_oracle_ns: ["newton_schulz"]}, test_oracle_ns.test_ns_equals_svd_closed_form, ((6, 12),)),
+    ("ns spectral norm instead of Frobenius",
+     [("frobenius_prescale", "return x / (math.sqrt(float(np.sum(x * x))) + eps)",
+       "return x / (float(np.linalg.norm(x, 2)) + eps)")], ["newton_schulz"],
+     {test_oracle_ns: ["newton_schulz", "frobenius_prescale"]}, test_oracle_ns.test_ns_equals_svd_closed_form,
+     ((16, 4),)),
+    ("momentum swaps mu and nu",
+     [("momentum_nesterov", "buf_new = _round_sum_of_products(mu, buf, nu, grad, storage)",
+       "buf_new = _round_sum_of_products(nu, buf, mu, grad, storage)")], [],
+     {test_oracle_momentum: ["momentum_nesterov"]}, test_oracle_momentum.test_momentum_is_exactly_rounded_bf16, ()),
+    ("u from the unrounded buffer",
+     [("momentum_nesterov", "u = _round_sum_of_products(nu, grad, mu, buf_new, BF16)",
+       "u = _round_sum_of_products(nu, grad, mu, np.asarray(mu) * np.asarray(buf) + np.asarray(nu) * "
+       "np.asarray(grad), BF16)")], [],
+     {test_oracle_momentum: ["momentum_nesterov"]}, test_oracle_momentum.test_momentum_is_exactly_rounded_bf16, ()),
+    ("bf16 rounding truncates",
+     [("round_to_format", "y = np.rint(x / quantum) * quantum", "y = np.trunc(x / quantum) * quantum")],
+     ["round_to_bf16"],
+     {test_oracle_rounding: ["round_to_bf16"]}, test_oracle_rounding.test_bf16_rounding_matches_brute_force_search,
+     ()),
+    ("the split rounds instead of slicing",
+     [("split", "return (bits >> np.uint32(16)).astype(np.uint16), (bits & np.uint32(0xFFFF)).astype(np.uint16)",
+       "return ((bits + np.uint32(0x8000)) >> np.uint32(16)).astype(np.uint16), "
+       "(bits & np.uint32(0xFFFF)).astype(np.uint16)")], [],
+     {test_oracle_apply: ["split"]}, test_oracle_apply.test_split_is_a_bit_slice, ()),
+    ("the apply drops the decay",
+     [("mp_apply_update", "t = round_to_f32(w * np.asarray(decay, dtype=np.float64))", "t = w")], [],
+     {test_oracle_apply: ["mp_apply_update"]}, test_oracle_apply.test_apply_is_exactly_rounded_on_random_inputs, ()),
+    ("per-slot eta not rounded to float32",
+     [("muon_bank_step", "eta = round_to_f32(sc.eta * per)[:, None, None]", "eta = (sc.eta * per)[:, None, None]")],
+     [], {test_oracle_step: ["muon_bank_step"]}, test_oracle_step.test_per_slot_eta_is_one_fp32_multiply, ()),
+    ("step reads u from the unrounded buffer",
+     [("momentum_nesterov", "u = _round_sum_of_products(nu, grad, mu, buf_new, BF16)",
+       "u = _round_sum_of_products(nu, grad, mu, np.asarray(mu) * np.asarray(buf) + np.asarray(nu) * "
+       "np.asarray(grad), BF16)")], ["muon_bank_step"],
+     {test_oracle_step: ["muon_bank_step"]}, test_oracle_step.test_nesterov_reads_the_stored_buffer, ()),
+]
+
+
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_pin_catches_planted_mistake(case, monkeypatch):
+    _, edits, rebuild, bind, pin, args = case
+    ns = mutant(edits, rebuild)
+    for module, names in bind.items():
+        for name in names:
+            monkeypatch.setattr(module, name, ns[name])
+    with pytest.raises(AssertionError):
+        pin(*args)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_the_unedited_oracle_passes_the_same_pin(case):
+    """Control: the pin passes with the oracle as it is (re-executed the same way, with no edit)."""
+    _, edits, rebuild, bind, pin, args = case
+    ns = mutant([], [e[0] for e in edits] + list(rebuild))
+    with pytest.MonkeyPatch.context() as mp:
+        for module, names in bind.items():
+            for name in names:
+                mp.setattr(module, name, ns[name])
+        pin(*args)
