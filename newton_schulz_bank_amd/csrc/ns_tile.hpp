@@ -24,6 +24,8 @@
 // data written during the same kernel by another CU of the same XCD needs.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace mb {
@@ -270,22 +272,29 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, lds_u16* smem, int 
     for (int b = 0; b < C::FN; ++b)
         qf[0][b] = read_frag_fast<Q_KMAJOR, C::BN>(qslot(0, 0), wn * C::TN + b * 32, 0, lane);
 
+    // One ring stage.  The last stage is a separate instantiation: were both kinds one loop body, the
+    // compiler would merge the path that read the next stage's first fragments after the barrier with
+    // the path that did not, and wait for those reads before the last MFMAs of the stage (every
+    // wavefront of the workgroup, just past the barrier, would then leave its SIMD idle for the LDS
+    // latency of the whole workgroup's reads).
     int s3 = 0;                                          // kt % NPS
-    for (int kt = 0; kt < KT; ++kt) {
+    auto stage = [&](int kt, auto has_next) {
+        constexpr bool more = decltype(has_next)::value;
         const int s2 = kt & 1;
         const int n3 = s3 + 1 == C::NPS ? 0 : s3 + 1;    // (kt + 1) % NPS
         const lds_u16* lp = pslot(s3, s2);
         const lds_u16* lq = qslot(s3, s2);
-        const bool more = kt + 1 < KT;
         // the slots of stage kt - 1 are free (every wave passed the barrier after reading them)
         bool ahead = false;
-        if (C::PAHEAD) {
-            if (more) copy_other(kt + 1, s2 ^ 1);
-            ahead = kt + 2 < KT;
-            if (ahead) copy_ahead(kt + 2, n3 + 1 == C::NPS ? 0 : n3 + 1);
-        } else if (more) {
-            copy_ahead(kt + 1, n3);
-            copy_other(kt + 1, s2 ^ 1);
+        if constexpr (more) {
+            if (C::PAHEAD) {
+                copy_other(kt + 1, s2 ^ 1);
+                ahead = kt + 2 < KT;
+                if (ahead) copy_ahead(kt + 2, n3 + 1 == C::NPS ? 0 : n3 + 1);
+            } else {
+                copy_ahead(kt + 1, n3);
+                copy_other(kt + 1, s2 ^ 1);
+            }
         }
 #pragma unroll
         for (int kk = 0; kk < kBK / 16; ++kk) {
@@ -297,7 +306,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, lds_u16* smem, int 
 #pragma unroll
                 for (int b = 0; b < C::FN; ++b)
                     qf[nb][b] = read_frag_fast<Q_KMAJOR, C::BN>(lq, wn * C::TN + b * 32, kk + 1, lane);
-            } else if (more) {
+            } else if constexpr (more) {
                 // every wave's reads of this stage are done and the next stage has landed (with the
                 // three-slot ring, the copy of stage kt + 2's ahead operand, issued last, may still be
                 // in flight)
@@ -322,7 +331,9 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, lds_u16* smem, int 
             __builtin_amdgcn_sched_barrier(0);
         }
         s3 = n3;
-    }
+    };
+    for (int kt = 0; kt + 1 < KT; ++kt) stage(kt, std::true_type{});
+    if (KT > 0) stage(KT - 1, std::false_type{});
 
     // ---- epilogue, staged through LDS so that every global access is a full coalesced row:
     //   1. (polynomial, update) the aux tile A or X is copied into LDS with buffer_load ... lds;
