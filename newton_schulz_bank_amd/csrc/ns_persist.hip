@@ -6,7 +6,7 @@
 //     A = G^T G,   B as above,        G' = a*G + G B      (tall G),
 // and the slots are independent.  Instead of one launch per contraction (whose
 // last wave of tiles leaves most CUs idle and whose boundary writes back the
-// whole L2), every 256x256 output tile of every contraction of every bank is a
+// whole L2), every 256x256 (or 128x128) output tile of every contraction of every bank is a
 // task, and the workgroups of one launch take tasks from a queue while they
 // last: the short contractions of one bank fill the gaps of another's.
 //
