@@ -208,8 +208,33 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, lds_u16* smem, int 
     const int lane = tid & 63;
     // the wavefront's index is uniform: in scalar registers, its row and column offsets cost no VGPRs
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / C::WN, wn = wave % C::WN;
     const int i0 = jb.i0, j0 = jb.j0;
+    // a diagonal tile of a symmetric product (X X^T, A A) has P == Q: its operand is copied once
+    // and both fragment sets read it
+    const bool same = P_KMAJOR == Q_KMAJOR && C::BM == C::BN &&
+                      __builtin_amdgcn_readfirstlane((int)(i0 == j0 && jb.P[0] == jb.Q[0] && jb.P[1] == jb.Q[1] &&
+                                                           jb.ldp == jb.ldq)) != 0;
+    // Such a tile computes only the wavefront blocks on and above its diagonal, one per wavefront in
+    // row-major order (10 of 16 with a 4 x 4 grid; with the wavefronts placed on the four SIMDs in
+    // turn, at most three per SIMD instead of four, so its K-loop needs three quarters of the MFMA
+    // time), and stores the blocks below the diagonal as the
+    // transposes of those above it: the same bits, since a block below the diagonal holds the same
+    // exact bf16 products summed in the same order as its mirror image.  The other wavefronts copy
+    // and wait at the barriers but compute nothing.
+    // (256-tiles only: the 128-tiles serve short chains, whose tasks gain less than the transposing
+    // stores and the second copy of the K-loop cost)
+    constexpr bool kTri = C::BM == 256 && C::WM == C::WN;
+    const bool tri = kTri && EPI != EPI_UPDATE && same;
+    int wm = wave / C::WN, wn = wave % C::WN;
+    bool active = true;
+    if constexpr (kTri) {
+        if (tri) {
+            active = wave < C::WM * (C::WM + 1) / 2;
+            if (active) sym_tile(wave, C::WM, wm, wn);
+            wm = __builtin_amdgcn_readfirstlane(wm);
+            wn = __builtin_amdgcn_readfirstlane(wn);
+        }
+    }
 
     f32x16 acc[C::FM][C::FN];
 #pragma unroll
@@ -220,11 +245,6 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, lds_u16* smem, int 
             for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
     const int KT = jb.K / kBK;
-    // a diagonal tile of a symmetric product (X X^T, A A) has P == Q: its operand is copied once
-    // and both fragment sets read it
-    const bool same = P_KMAJOR == Q_KMAJOR && C::BM == C::BN &&
-                      __builtin_amdgcn_readfirstlane((int)(i0 == j0 && jb.P[0] == jb.Q[0] && jb.P[1] == jb.Q[1] &&
-                                                           jb.ldp == jb.ldq)) != 0;
     // The ring: NPS slots of the operand copied ahead (P, or Q with QAHEAD; a diagonal tile copies
     // only P and always ahead), then two slots of the other.  Stage kt's operands sit in slot kt % NPS
     // of the first group and slot kt % 2 of the second.
@@ -265,12 +285,14 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, lds_u16* smem, int 
     // the MFMAs of step kk, and the first reads of the next stage right after the barrier,
     // ahead of the last MFMAs of the current one
     bf16x8 pf[2][C::FM], qf[2][C::FN];
+    if (active) {
 #pragma unroll
-    for (int a = 0; a < C::FM; ++a)
-        pf[0][a] = read_frag_fast<P_KMAJOR, C::BM>(pslot(0, 0), wm * C::TM + a * 32, 0, lane);
+        for (int a = 0; a < C::FM; ++a)
+            pf[0][a] = read_frag_fast<P_KMAJOR, C::BM>(pslot(0, 0), wm * C::TM + a * 32, 0, lane);
 #pragma unroll
-    for (int b = 0; b < C::FN; ++b)
-        qf[0][b] = read_frag_fast<Q_KMAJOR, C::BN>(qslot(0, 0), wn * C::TN + b * 32, 0, lane);
+        for (int b = 0; b < C::FN; ++b)
+            qf[0][b] = read_frag_fast<Q_KMAJOR, C::BN>(qslot(0, 0), wn * C::TN + b * 32, 0, lane);
+    }
 
     // One ring stage.  The last stage is a separate instantiation: were both kinds one loop body, the
     // compiler would merge the path that read the next stage's first fragments after the barrier with
@@ -278,8 +300,9 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, lds_u16* smem, int 
     // wavefront of the workgroup, just past the barrier, would then leave its SIMD idle for the LDS
     // latency of the whole workgroup's reads).
     int s3 = 0;                                          // kt % NPS
-    auto stage = [&](int kt, auto has_next) {
+    auto stage = [&](int kt, auto has_next, auto computes) {
         constexpr bool more = decltype(has_next)::value;
+        constexpr bool mf = decltype(computes)::value;   // false: an idle wavefront (copies and barriers only)
         const int s2 = kt & 1;
         const int n3 = s3 + 1 == C::NPS ? 0 : s3 + 1;    // (kt + 1) % NPS
         const lds_u16* lp = pslot(s3, s2);
@@ -300,12 +323,14 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, lds_u16* smem, int 
         for (int kk = 0; kk < kBK / 16; ++kk) {
             const int fb = kk & 1, nb = fb ^ 1;
             if (kk + 1 < kBK / 16) {
+                if constexpr (mf) {
 #pragma unroll
-                for (int a = 0; a < C::FM; ++a)
-                    pf[nb][a] = read_frag_fast<P_KMAJOR, C::BM>(lp, wm * C::TM + a * 32, kk + 1, lane);
+                    for (int a = 0; a < C::FM; ++a)
+                        pf[nb][a] = read_frag_fast<P_KMAJOR, C::BM>(lp, wm * C::TM + a * 32, kk + 1, lane);
 #pragma unroll
-                for (int b = 0; b < C::FN; ++b)
-                    qf[nb][b] = read_frag_fast<Q_KMAJOR, C::BN>(lq, wn * C::TN + b * 32, kk + 1, lane);
+                    for (int b = 0; b < C::FN; ++b)
+                        qf[nb][b] = read_frag_fast<Q_KMAJOR, C::BN>(lq, wn * C::TN + b * 32, kk + 1, lane);
+                }
             } else if constexpr (more) {
                 // every wave's reads of this stage are done and the next stage has landed (with the
                 // three-slot ring, the copy of stage kt + 2's ahead operand, issued last, may still be
@@ -315,25 +340,38 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, lds_u16* smem, int 
                 __builtin_amdgcn_s_barrier();
                 const lds_u16* np = pslot(n3, s2 ^ 1);
                 const lds_u16* nq = qslot(n3, s2 ^ 1);
+                if constexpr (mf) {
 #pragma unroll
-                for (int a = 0; a < C::FM; ++a)
-                    pf[nb][a] = read_frag_fast<P_KMAJOR, C::BM>(np, wm * C::TM + a * 32, 0, lane);
+                    for (int a = 0; a < C::FM; ++a)
+                        pf[nb][a] = read_frag_fast<P_KMAJOR, C::BM>(np, wm * C::TM + a * 32, 0, lane);
 #pragma unroll
-                for (int b = 0; b < C::FN; ++b)
-                    qf[nb][b] = read_frag_fast<Q_KMAJOR, C::BN>(nq, wn * C::TN + b * 32, 0, lane);
+                    for (int b = 0; b < C::FN; ++b)
+                        qf[nb][b] = read_frag_fast<Q_KMAJOR, C::BN>(nq, wn * C::TN + b * 32, 0, lane);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (mf) {
 #pragma unroll
-            for (int a = 0; a < C::FM; ++a)
+                for (int a = 0; a < C::FM; ++a)
 #pragma unroll
-                for (int b = 0; b < C::FN; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[fb][b], pf[fb][a], acc[a][b], 0, 0, 0);
+                    for (int b = 0; b < C::FN; ++b)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[fb][b], pf[fb][a], acc[a][b], 0, 0, 0);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
         s3 = n3;
     };
-    for (int kt = 0; kt + 1 < KT; ++kt) stage(kt, std::true_type{});
-    if (KT > 0) stage(KT - 1, std::false_type{});
+    // two copies of the loop, so that no branch on the wavefront's role sits inside it
+    auto kloop = [&](auto computes) {
+        for (int kt = 0; kt + 1 < KT; ++kt) stage(kt, std::true_type{}, computes);
+        if (KT > 0) stage(KT - 1, std::false_type{}, computes);
+    };
+    if constexpr (kTri) {
+        if (active) kloop(std::true_type{});
+        else kloop(std::false_type{});
+    } else {
+        kloop(std::true_type{});
+    }
 
     // ---- epilogue, staged through LDS so that every global access is a full coalesced row:
     //   1. (polynomial, update) the aux tile A or X is copied into LDS with buffer_load ... lds;
@@ -370,35 +408,38 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, lds_u16* smem, int 
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
     }
+    // (the idle wavefronts of a diagonal tile have no block)
+    if (active) {
 #pragma unroll
-    for (int a = 0; a < C::FM; ++a) {
-        const int i = wm * C::TM + a * 32 + (lane & 31);
+        for (int a = 0; a < C::FM; ++a) {
+            const int i = wm * C::TM + a * 32 + (lane & 31);
 #pragma unroll
-        for (int b = 0; b < C::FN; ++b) {
+            for (int b = 0; b < C::FN; ++b) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int j = wn * C::TN + b * 32 + 8 * g + 4 * (lane >> 5);
-                lds_u16* p = st + spos(i, j >> 3) + (j & 4);
-                float av[4] = {0.f, 0.f, 0.f, 0.f};
-                if (EPI != EPI_GRAM) {
-                    const u32x2 wv = *(const MB_LDS u32x2*)p;
-                    av[0] = __uint_as_float(wv[0] << 16);
-                    av[1] = __uint_as_float(wv[0] & 0xFFFF0000u);
-                    av[2] = __uint_as_float(wv[1] << 16);
-                    av[3] = __uint_as_float(wv[1] & 0xFFFF0000u);
+                for (int g = 0; g < 4; ++g) {
+                    const int j = wn * C::TN + b * 32 + 8 * g + 4 * (lane >> 5);
+                    lds_u16* p = st + spos(i, j >> 3) + (j & 4);
+                    float av[4] = {0.f, 0.f, 0.f, 0.f};
+                    if (EPI != EPI_GRAM) {
+                        const u32x2 wv = *(const MB_LDS u32x2*)p;
+                        av[0] = __uint_as_float(wv[0] << 16);
+                        av[1] = __uint_as_float(wv[0] & 0xFFFF0000u);
+                        av[2] = __uint_as_float(wv[1] << 16);
+                        av[3] = __uint_as_float(wv[1] & 0xFFFF0000u);
+                    }
+                    float y[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float x = acc[a][b][4 * g + r];
+                        if (EPI == EPI_GRAM) y[r] = jb.sig * x;
+                        else if (EPI == EPI_POLY) y[r] = __fmaf_rn(jb.beta, av[r], jb.alpha * x);
+                        else y[r] = jb.sig * __fmaf_rn(jb.beta, av[r], x);
+                    }
+                    u32x2 wv;
+                    wv[0] = f32x2_to_bf16x2_rne(y[0], y[1]);
+                    wv[1] = f32x2_to_bf16x2_rne(y[2], y[3]);
+                    *(MB_LDS u32x2*)p = wv;
                 }
-                float y[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float x = acc[a][b][4 * g + r];
-                    if (EPI == EPI_GRAM) y[r] = jb.sig * x;
-                    else if (EPI == EPI_POLY) y[r] = __fmaf_rn(jb.beta, av[r], jb.alpha * x);
-                    else y[r] = jb.sig * __fmaf_rn(jb.beta, av[r], x);
-                }
-                u32x2 wv;
-                wv[0] = f32x2_to_bf16x2_rne(y[0], y[1]);
-                wv[1] = f32x2_to_bf16x2_rne(y[2], y[3]);
-                *(MB_LDS u32x2*)p = wv;
             }
         }
     }
@@ -407,10 +448,11 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, lds_u16* smem, int 
 #pragma unroll
     for (int v = tid; v < CH; v += C::NT) {
         const int i = v / CPRO, c = v % CPRO;
+        if (tri && i / C::TM > c * 8 / C::TN) continue;     // below the diagonal: stored transposed below
         *reinterpret_cast<u32x4*>(jb.out + (int64_t)(i0 + i) * jb.ldo + j0 + c * 8) =
             *(const MB_LDS u32x4*)(st + spos(i, c));
     }
-    if (EPI != EPI_UPDATE && jb.mirror) {
+    if (EPI != EPI_UPDATE && (jb.mirror || tri)) {
         // unit (ib, jb16): tile rows [32 ib, 32 ib + 32) x columns [16 jb16, 16 jb16 + 16); the four
         // 16-lane groups of a wave take 8 rows each.  In a group, lane 4s + q addresses row s
         // (then s + 4) at columns 4q..4q+3, and lane t receives column t of those rows: elements
@@ -421,6 +463,8 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, lds_u16* smem, int 
 #pragma unroll
         for (int u = wave; u < UNITS; u += C::NW) {
             const int ib = u % (C::BM / 32), jb16 = u / (C::BM / 32);
+            // a diagonal tile transposes only its blocks above the diagonal, into those below it
+            if (tri && ib * 32 / C::TM >= jb16 * 16 / C::TN) continue;
             const int i = ib * 32 + grp * 8;
             const int jc = jb16 * 16 + 4 * q4;
             const lds_u16* pa = st + spos(i + s4, jc >> 3) + (jc & 7);
