@@ -217,12 +217,11 @@ __device__ __forceinline__ void gemm_tile(const TileJob& jb, lds_u16* smem, int 
     // Such a tile computes only the wavefront blocks on and above its diagonal, one per wavefront in
     // row-major order (10 of 16 with a 4 x 4 grid; with the wavefronts placed on the four SIMDs in
     // turn, at most three per SIMD instead of four, so its K-loop needs three quarters of the MFMA
-    // time), and stores the blocks below the diagonal as the
-    // transposes of those above it: the same bits, since a block below the diagonal holds the same
-    // exact bf16 products summed in the same order as its mirror image.  The other wavefronts copy
-    // and wait at the barriers but compute nothing.
-    // (256-tiles only: the 128-tiles serve short chains, whose tasks gain less than the transposing
-    // stores and the second copy of the K-loop cost)
+    // time), and stores the blocks below the diagonal as the transposes of those above it.  These are
+    // the same bits: a block below the diagonal holds the same exact bf16 products, summed in the same
+    // order, as its mirror image, and the polynomial's aux A is symmetric.  The other wavefronts copy
+    // and wait at the barriers but compute nothing.  (256-tiles only: the 128-tiles serve short
+    // chains, whose tasks gain less than the transposing stores and the second copy of the K-loop cost.)
     constexpr bool kTri = C::BM == 256 && C::WM == C::WN;
     const bool tri = kTri && EPI != EPI_UPDATE && same;
     int wm = wave / C::WN, wn = wave % C::WN;
