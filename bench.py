@@ -95,14 +95,14 @@ def main():
         return
     sys.path.insert(0, HERE)
     from newton_schulz_bank_amd import api
-    from newton_schulz_bank_amd.workloads import CONFIG_NAMES, CONFIGS, make_bank
+    from newton_schulz_bank_amd.workloads import WORKLOAD_NAMES, WORKLOADS, make_bank
 
     api.lib()    # fails loudly if libmuonbank.so is missing
     if args.workload == "transpose":
         bench_transpose(args, torch, api)
         return
     api.mb_ns_set_path(args.ns_path)
-    specs = CONFIGS[args.config]
+    specs = WORKLOADS[args.config]
     hosts = [make_bank(args.config, i) for i in range(len(specs))]
 
     def upload():
@@ -257,7 +257,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": CONFIG_NAMES[args.config], "config_id": args.config,
+        "config": {"workload": WORKLOAD_NAMES[args.config], "config_id": args.config,
                    "banks": [[s.batch, s.rows, s.cols] for s in specs], "live_slots": live_slots,
                    "ns_steps": 5, "grad_dtype": specs[0].grad_dtype, "ns_path": args.ns_path},
         "matrices_per_s": round(live_slots / (ms_per_step * 1e-3), 1),

@@ -69,7 +69,7 @@ def _attn(batch=40, d=768):
     return BankSpec("attn_qkvo", batch, d, d)
 
 
-CONFIGS: dict[int, list[BankSpec]] = {
+WORKLOADS: dict[int, list[BankSpec]] = {
     0: [BankSpec("fp32_256", 4, 256, 256, grad_dtype="f32", grad_scale=1.0, mom_scale=None,
                  lo_uniform=False)],
     1: [_attn()],
@@ -92,7 +92,7 @@ CONFIGS: dict[int, list[BankSpec]] = {
         BankSpec("mlp_2816", 24, 2816, 768, grad_dist="student_t3", dead_slots=(7,), seed_config=4)],
 }
 
-CONFIG_NAMES = {
+WORKLOAD_NAMES = {
     0: "4x256x256 fp32 grads, zero momentum",
     1: "attention QKVO bank (10,3072,768) viewed (40,768,768)",
     2: "MLP bank (12,2,3072,768) viewed (24,3072,768), slot 23 dead",
@@ -136,7 +136,7 @@ def make_bank(config: int, bank: int, spec: BankSpec | None = None, slots=None) 
     for fp32 banks), ``w_hi`` (uint16 bf16 weight bits) and ``w_lo`` (uint16
     low mantissas), each of shape [batch, rows, cols].  ``slots`` (optional)
     keeps only the listed slots of the full draw, for small samples of big banks."""
-    spec = spec or CONFIGS[config][bank]
+    spec = spec or WORKLOADS[config][bank]
     shape = (spec.batch, spec.rows, spec.cols)
     sc = config if spec.seed_config is None else spec.seed_config
     g64 = _sample(_rng(sc, bank, GRAD), spec.grad_dist, spec.grad_scale, shape)

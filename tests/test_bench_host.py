@@ -11,7 +11,7 @@ import pytest
 
 import bench
 import oracle
-from newton_schulz_bank_amd.workloads import CONFIGS, make_bank
+from newton_schulz_bank_amd.workloads import WORKLOADS, make_bank
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -52,7 +52,7 @@ def _oracle_sample(spec, h):
 
 
 def test_sample_comparison_accepts_a_correct_step_and_rejects_a_flipped_bit():
-    spec = CONFIGS[1][0]                    # the attention bank; its slot 0 is live
+    spec = WORKLOADS[1][0]                    # the attention bank; its slot 0 is live
     h = make_bank(1, 0, slots=[0])
     sample = _oracle_sample(spec, h)
     got = bench._sample_parity(oracle, spec, h, sample)

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 from newton_schulz_bank_amd import api
-from newton_schulz_bank_amd.workloads import CONFIGS, make_bank
+from newton_schulz_bank_amd.workloads import WORKLOADS, make_bank
 from tests.gpu_util import bits, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -27,7 +27,7 @@ def say(msg):
 
 def _banks(config):
     out = []
-    for i, spec in enumerate(CONFIGS[config]):
+    for i, spec in enumerate(WORKLOADS[config]):
         h = make_bank(config, i)
         bf = spec.grad_dtype == "bf16"
         out.append((h, bf))

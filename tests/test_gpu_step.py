@@ -20,7 +20,7 @@ import torch
 
 import oracle
 from newton_schulz_bank_amd import api
-from newton_schulz_bank_amd.workloads import CONFIGS, make_bank
+from newton_schulz_bank_amd.workloads import WORKLOADS, make_bank
 from tests.gpu_util import bits, rel_fro, to_dev, vals
 
 pytestmark = pytest.mark.gpu
@@ -62,11 +62,11 @@ def say(msg):
 
 @functools.lru_cache(maxsize=2)
 def host_inputs(config):
-    return tuple(make_bank(config, i) for i in range(len(CONFIGS[config])))
+    return tuple(make_bank(config, i) for i in range(len(WORKLOADS[config])))
 
 
 def _upload(config):
-    specs = CONFIGS[config]
+    specs = WORKLOADS[config]
     banks = []
     for spec, h in zip(specs, host_inputs(config)):
         bf = spec.grad_dtype == "bf16"
@@ -79,7 +79,7 @@ def _upload(config):
 
 
 def _run(config):
-    specs = CONFIGS[config]
+    specs = WORKLOADS[config]
     banks = _upload(config)
     api.muon_bank_step(banks)
     torch.cuda.synchronize()
@@ -165,7 +165,7 @@ def _check_paths_bitwise(config, banks0):
     finally:
         api.mb_ns_set_path(prev)
     checked = 0
-    for spec, a, b in zip(CONFIGS[config], first, second):
+    for spec, a, b in zip(WORKLOADS[config], first, second):
         if spec.rows % 128 or spec.cols % 128:
             continue                      # small and ragged slots take other kernels on the two paths
         for name, x, y in zip(("v", "w_hi", "w_lo"), a, b):
@@ -182,7 +182,7 @@ def test_slot_scalar_table_matches_oracle():
     own scalars, the apply bit-exact on the GPU's v, Newton-Schulz within the tolerance on sampled slots."""
     say("bank step with a per-slot scalar table")
     config = 3
-    specs, host = CONFIGS[config], host_inputs(config)
+    specs, host = WORKLOADS[config], host_inputs(config)
     banks = _upload(config)
     table = api.slot_scalars_table(banks)
     rng = np.random.default_rng(123)
@@ -263,7 +263,7 @@ def test_per_slot_lr_and_multipliers():
 
 def _fresh_bank(config, index):
     h = make_bank(config, index)
-    bf = CONFIGS[config][index].grad_dtype == "bf16"
+    bf = WORKLOADS[config][index].grad_dtype == "bf16"
     b = api.Bank(grad=to_dev(h["grad"], bf), momentum=to_dev(h["momentum"], bf), w_hi=to_dev(h["w_hi"]),
                  w_lo=to_dev(h["w_lo"]))
     b.v_out = torch.empty(h["w_hi"].shape, dtype=torch.int16, device="cuda")

@@ -6,7 +6,7 @@ import numpy as np
 
 from oracle import BF16, F32, bf16_bits_to_f64, mp_apply_update, muon_bank_step, newton_schulz, recombine, \
     round_fraction, round_to_bf16, step_scalars
-from newton_schulz_bank_amd.workloads import CONFIGS, make_bank, make_random_bank
+from newton_schulz_bank_amd.workloads import WORKLOADS, make_bank, make_random_bank
 
 
 def _vals(bank, key, dtype):
@@ -96,7 +96,7 @@ def test_fp32_config_zero_momentum_closed_form():
     out = muon_bank_step(g, np.zeros_like(g), bank["w_hi"], bank["w_lo"], F32)
     sc = out["scalars"]
     np.testing.assert_array_equal(out["momentum"], (sc.nu * g).astype(np.float32).astype(np.float64))
-    assert CONFIGS[0][0].grad_dtype == "f32"
+    assert WORKLOADS[0][0].grad_dtype == "f32"
 
 
 def test_slot_scalar_table_is_applied_per_slot_exactly():

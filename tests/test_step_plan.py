@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 from newton_schulz_bank_amd import api
-from newton_schulz_bank_amd.workloads import CONFIGS
+from newton_schulz_bank_amd.workloads import WORKLOADS
 
 
 @pytest.fixture(scope="module")
@@ -42,10 +42,10 @@ def plan(L, shapes, xcds=8, hp=None, cus=None):
 
 
 def shapes_of(config):
-    return [(s.batch, s.rows, s.cols) for s in CONFIGS[config]]
+    return [(s.batch, s.rows, s.cols) for s in WORKLOADS[config]]
 
 
-@pytest.mark.parametrize("config", sorted(CONFIGS))
+@pytest.mark.parametrize("config", sorted(WORKLOADS))
 @pytest.mark.parametrize("xcds", [8, 1, 3, 6, 16])
 def test_every_workload_plans_and_its_task_lists_check(L, config, xcds):
     plan(L, shapes_of(config), xcds)
