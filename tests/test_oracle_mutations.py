@@ -15,16 +15,20 @@ import inspect
 import pytest
 
 import oracle.muon as om
-from tests import test_oracle_apply, test_oracle_momentum, test_oracle_ns, test_oracle_rounding, test_oracle_step
+import oracle.transpose as ot
+from tests import (test_oracle_apply, test_oracle_momentum, test_oracle_ns, test_oracle_rounding, test_oracle_step,
+                   test_oracle_transpose)
 
 
 def mutant(edits, rebuild):
-    """Namespace copy of oracle.muon in which `edits` [(function, old line text, new text)] are applied
-    and every function in `rebuild` is re-executed, so that they call the edited ones."""
-    ns = dict(om.__dict__)
+    """Namespace copy of the oracle module that defines the edited functions (oracle.muon or
+    oracle.transpose) in which `edits` [(function, old line text, new text)] are applied and every
+    function in `rebuild` is re-executed, so that they call the edited ones."""
     names = list(dict.fromkeys([e[0] for e in edits] + list(rebuild)))
+    mod = om if hasattr(om, names[0]) else ot
+    ns = dict(mod.__dict__)
     for name in names:
-        src = inspect.getsource(getattr(om, name))
+        src = inspect.getsource(getattr(mod, name))
         for fn, old, new in edits:
             if fn == name:
                 assert old in src, f"{name}: the line to edit is gone from the oracle: {old!r}"
@@ -77,6 +81,16 @@ CASES = [
     ("per-slot eta not rounded to float32",
      [("muon_bank_step", "eta = round_to_f32(sc.eta * per)[:, None, None]", "eta = (sc.eta * per)[:, None, None]")],
      [], {test_oracle_step: ["muon_bank_step"]}, test_oracle_step.test_per_slot_eta_is_one_fp32_multiply, ()),
+    ("transpose_copy reverses the row order",
+     [("transpose_copy", "out[:, i] = src[i, :]", "out[:, i] = src[rows - 1 - i, :]")], [],
+     {test_oracle_transpose: ["transpose_copy"]}, test_oracle_transpose.test_copy_is_the_transpose_by_brute_force_and_numpy,
+     ()),
+    ("transpose_add reshapes src instead of transposing it",
+     [("transpose_add", "src_t = transpose_copy(src)", "src_t = np.asarray(src).reshape(dst.shape)")], [],
+     {test_oracle_transpose: ["transpose_add"]}, test_oracle_transpose.test_add_f32_is_the_correctly_rounded_sum, ()),
+    ("transpose_add leaves the float32 sum unrounded",
+     [("transpose_add", "return round_to_f32(s).astype(np.float32)", "return s")], [],
+     {test_oracle_transpose: ["transpose_add"]}, test_oracle_transpose.test_add_f32_is_the_correctly_rounded_sum, ()),
     ("step reads u from the unrounded buffer",
      [("momentum_nesterov", "u = _round_sum_of_products(nu, grad, mu, buf_new, BF16)",
        "u = _round_sum_of_products(nu, grad, mu, np.asarray(mu) * np.asarray(buf) + np.asarray(nu) * "
