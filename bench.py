@@ -62,15 +62,61 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-parity", action="store_true")
     p.add_argument("--no-probes", action="store_true", help="skip the measured-peak probes")
-    p.add_argument("--workload", default="bank", choices=("bank", "transpose"),
+    p.add_argument("--workload", default="bank", choices=("bank", "transpose", "vendor-gemm"),
                    help="bank: the Muon bank step (the headline); transpose: the tied-embedding transposes of "
-                        "one optimizer step at the LM-head size")
+                        "one optimizer step at the LM-head size; vendor-gemm: the vendor library's dense bf16 "
+                        "batched products (torch.bmm) on the shapes of the Newton-Schulz contractions, for "
+                        "comparison only")
     p.add_argument("--ns-path", type=int, default=0, choices=(0, 1),
                    help="0: persistent Newton-Schulz kernel where the shape allows it; 1: one launch per contraction")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run one device-to-device copy of MIB MiB (the known-size reference that the "
                         "FETCH_SIZE / WRITE_SIZE counters of the kernels are scaled by) and exit")
     return p.parse_args()
+
+
+# Dense products with the shapes of the Newton-Schulz contractions (batch, m, k, n): X Xᵀ or Gᵀ G, A·A and the
+# update of each bank, as plain batched products with every output computed, and one large square product.
+VENDOR_GEMM_SHAPES = [
+    ("attention bank 40 x 768^2: Gram, polynomial and update", 40, 768, 768, 768),
+    ("MLP bank 24 x 3072x768: Gram (k = 3072)", 24, 768, 3072, 768),
+    ("MLP bank 24 x 3072x768: update (3072 x 768 by 768 x 768)", 24, 3072, 768, 768),
+    ("350M attention 96 x 1024^2: Gram, polynomial and update", 96, 1024, 1024, 1024),
+    ("350M MLP 48 x 4096x1024: Gram (k = 4096)", 48, 1024, 4096, 1024),
+    ("350M MLP 48 x 4096x1024: update (4096 x 1024 by 1024 x 1024)", 48, 4096, 1024, 1024),
+    ("single 8192^3", 1, 8192, 8192, 8192),
+]
+
+
+def bench_vendor_gemm(args, torch):
+    """torch.bmm (the vendor BLAS) in bf16 on contiguous operands, each shape timed over back-to-back calls
+    between two events after warm-up; dense flops 2*b*m*k*n.  A comparison for the Newton-Schulz launch, not
+    part of the step."""
+    out = []
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    for name, b, m, k, n in VENDOR_GEMM_SHAPES:
+        x = torch.randn((b, m, k), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        y = torch.randn((b, k, n), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        x, y = x.contiguous(), y.contiguous()
+        for _ in range(max(args.warmup, 3)):
+            torch.bmm(x, y)
+        reps = max(args.steps, 10)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(reps):
+            torch.bmm(x, y)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / reps
+        tf = 2.0 * b * m * k * n / (ms * 1e-3) / 1e12
+        out.append({"shape": name, "batch": b, "m": m, "k": k, "n": n, "ms": round(ms, 4),
+                    "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+        print(f"vendor gemm {name}: {ms:.4f} ms, {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        del x, y
+    print(json.dumps({"metric": "vendor bf16 batched GEMM (torch.bmm) on the Newton-Schulz contraction shapes",
+                      "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS, "reps": max(args.steps, 10),
+                      "results": out}), flush=True)
 
 
 def main():
@@ -84,6 +130,9 @@ def main():
     import torch
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU (HIP device)")
+    if args.workload == "vendor-gemm":
+        bench_vendor_gemm(args, torch)
+        return
     if args.copy_calibration:
         n = args.copy_calibration << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
