@@ -246,11 +246,25 @@ int32_t mb_ns_set_path(int32_t path);
  * task of that launch waits for the previous contraction of its slot; the wait
  * gives up after 200 ms (no correct schedule comes near it), the launch then
  * finishes with undefined values in the affected slots, and this flag is set.
+ * It is also set when a launch ends with tasks of some XCD queue never claimed
+ * (a queue no workgroup served).
  * Returns 1 if any launch on the device has set it since it was last cleared, 0
  * if none has, -1 on a HIP error (detail in mb_last_error()); clears it when
  * `clear` is nonzero.  Blocking: it reads device memory on the null stream, so
  * call it after synchronizing the streams the steps were enqueued on. */
 int32_t mb_device_fault(int32_t clear);
+
+/* Test hook (for tests of the two failure paths above; not for use in a
+ * step): wait_cap_ticks > 0 replaces the 200 ms cap of a dependency wait
+ * (ticks of the 100 MHz constant clock; 1 gives up a wait at its first timed
+ * check), and extra_queues > 0 (at most 8) adds that many XCD queues beyond the
+ * device's XCDs: no workgroup serves them, so their slots' tasks never run and
+ * the launch's drain check reports them.  Either way the launch still finishes
+ * (nothing waits for a task of an unserved queue), sets the fault flag, and
+ * leaves undefined values in the affected slots.  Zero for both restores the
+ * defaults.  Process-wide, host only; applies to launches enqueued after the
+ * call.  MB_ERR_VALUE for a negative cap or extra_queues outside 0..8. */
+mb_status mb_test_persist_faults(int64_t wait_cap_ticks, int32_t extra_queues);
 
 /* Kernel timing (off by default).  While enabled, every kernel the library
  * launches is bracketed by two hipEvents on its stream; mb_timing_read waits

@@ -68,7 +68,8 @@ _lib = None
 EXPORTED = ("mb_default_hparams", "mb_status_string", "mb_last_error", "mb_version", "mb_slot_scalars_fill",
             "mb_step_plan", "mb_step_workspace_bytes",
             "mb_ns_workspace_bytes", "muon_bank_step", "muon_momentum_update", "ns_orthogonalize_batched",
-            "ns_orthogonalize_batched_sched", "ns_orthogonalize_batched_noalloc", "mp_apply_update", "transpose_copy", "transpose_add", "mb_ns_set_path", "mb_device_fault", "mb_timing_enable", "mb_timing_read")
+            "ns_orthogonalize_batched_sched", "ns_orthogonalize_batched_noalloc", "mp_apply_update", "transpose_copy", "transpose_add", "mb_ns_set_path", "mb_device_fault", "mb_test_persist_faults", "mb_timing_enable",
+            "mb_timing_read")
 
 
 def lib() -> ctypes.CDLL:
@@ -99,6 +100,7 @@ def lib() -> ctypes.CDLL:
         "mp_apply_update": (i32, [vp, vp, vp, i64, i64, f32, f32, vp, vp]),
         "mb_ns_set_path": (i32, [i32]),
         "mb_device_fault": (i32, [i32]),
+        "mb_test_persist_faults": (i32, [i64, i32]),
         "transpose_copy": (i32, [vp, vp, i64, i64, i32, vp]),
         "transpose_add": (i32, [vp, vp, i64, i64, i32, vp]),
         "mb_timing_enable": (None, [i32]),
@@ -395,6 +397,12 @@ def mb_device_fault(clear: bool = False) -> bool:
     if r < 0:
         raise MuonBankError(8, lib().mb_last_error().decode())
     return r == 1
+
+
+def mb_test_persist_faults(wait_cap_ticks: int = 0, extra_queues: int = 0) -> None:
+    """Test hook for the persistent launch's failure paths (tests only): a dependency-wait cap in ticks of
+    the 100 MHz constant clock (0: the default 200 ms) and extra XCD queues that no workgroup serves."""
+    _check(lib().mb_test_persist_faults(int(wait_cap_ticks), int(extra_queues)))
 
 
 def mb_timing_enable(on: bool) -> None:

@@ -143,6 +143,9 @@ bool ns_persist_check(const NsPersistBank* banks, int nbanks, int tile, int step
 // The current device's persistent-launch fault flag (1: a dependency wait hit its time cap since the
 // flag was last cleared); blocking; clears it when `clear` is set.
 hipError_t ns_persist_fault(int* flag, bool clear);
+// Test hook for the failure paths of the persistent launch: a dependency-wait cap in constant-clock ticks
+// (0: the default 200 ms) and a number of extra queues that no XCD serves (0: none).  Process-wide.
+void ns_persist_test_faults(uint64_t wait_cap_ticks, int extra_queues);
 
 // Every Newton-Schulz round of banks of small slots (Gram side <= 64, <= 4096 elements) in one launch
 // per kMaxSmallBanks banks, one workgroup per slot (x0 -> dest; dest may equal x0).

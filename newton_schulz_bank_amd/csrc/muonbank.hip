@@ -869,6 +869,14 @@ int32_t mb_device_fault(int32_t clear) {
     return flag != 0 ? 1 : 0;
 }
 
+mb_status mb_test_persist_faults(int64_t wait_cap_ticks, int32_t extra_queues) {
+    if (wait_cap_ticks < 0 || extra_queues < 0 || extra_queues > 8)
+        return fail(MB_ERR_VALUE, "mb_test_persist_faults: wait cap %lld, extra queues %d", (long long)wait_cap_ticks,
+                    extra_queues);
+    mb::ns_persist_test_faults((uint64_t)wait_cap_ticks, extra_queues);
+    return MB_OK;
+}
+
 void mb_timing_enable(int32_t on) {
     std::lock_guard<std::mutex> lk(g_timing_mu);
     g_timing_on = on != 0;

@@ -31,6 +31,7 @@
 // gives up instead of spinning forever.  The last workgroup to leave checks that
 // every queue was drained (a queue that no workgroup served would leave its
 // tasks undone) and sets the error word otherwise.
+#include <atomic>
 #include <cstdio>
 #include <vector>
 
@@ -48,6 +49,9 @@ __device__ int g_persist_fault;
 namespace {
 
 constexpr uint64_t kWaitCapTicks = 20000000;   // 200 ms of the 100 MHz constant clock
+// test hook (ns_persist_test_faults): a shorter wait cap, and queues beyond the XCDs that nothing serves
+std::atomic<uint64_t> g_test_wait_cap{0};
+std::atomic<int> g_test_extra_queues{0};
 // A 256-tile launch takes the three-slot ring from this many bytes of X (all slots of all its banks) on
 constexpr int64_t kAheadMinBytes = (int64_t)128 << 20;
 // Tasks of one round per queue, in units of the queue's workgroups, from which a launch claims early
@@ -116,7 +120,7 @@ __global__ void __launch_bounds__(C::NT, 2) ns_persist_kernel(PersistArgs p) {
                 __builtin_amdgcn_s_sleep(2);
                 if (__builtin_amdgcn_readfirstlane(ld_relaxed(ctr)) >= need) break;
                 if ((spin & 63) == 63 && (__builtin_amdgcn_readfirstlane(ld_relaxed(p.err)) != 0 ||
-                                          wall_clock64() - t0 > kWaitCapTicks)) {
+                                          wall_clock64() - t0 > p.wait_cap)) {
                     __hip_atomic_store(p.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     __hip_atomic_store(&g_persist_fault, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
                     break;
@@ -287,6 +291,11 @@ hipError_t device_shape(DeviceShape* out) {
 
 }  // namespace
 
+void ns_persist_test_faults(uint64_t wait_cap_ticks, int extra_queues) {
+    g_test_wait_cap.store(wait_cap_ticks);
+    g_test_extra_queues.store(extra_queues);
+}
+
 hipError_t ns_persist_fault(int* flag, bool clear) {
     hipError_t e = hipMemcpyFromSymbol(flag, HIP_SYMBOL(g_persist_fault), sizeof(int), 0, hipMemcpyDeviceToHost);
     if (e != hipSuccess || !clear || *flag == 0) return e;
@@ -423,10 +432,16 @@ hipError_t ns_persist(const NsPersistBank* banks, int nbanks, int tile, const Ns
     hipError_t e = device_shape(&d);
     if (e != hipSuccess) return e;
     if (!d.understood) return hipErrorNotSupported;
+    // (the test hook's extra queues take the slots g with g % nq >= the XCD count: no workgroup serves
+    // them, so they never run, nothing waits for them, and the drain check reports them)
+    const int nq = d.xccs + g_test_extra_queues.load();
+    if (nq > kMaxQueues) return hipErrorInvalidValue;
     PersistArgs p{};
-    fill_persist_args(p, banks, nbanks, tile, coef, steps, d.xccs, sync);
+    fill_persist_args(p, banks, nbanks, tile, coef, steps, nq, sync);
     const PersistLaunch l = launch_of(p, banks, nbanks, tile, d.cus, d.xccs);
     p.claim_early = l.claim_early;
+    const uint64_t cap = g_test_wait_cap.load();
+    p.wait_cap = cap ? cap : kWaitCapTicks;
     const dim3 grid((unsigned)(l.wg_per_queue * d.xccs));
     if (tile == 256 && l.ring == 3)
         ns_persist_kernel<Cfg256><<<grid, Cfg256::NT, 0, stream>>>(p);

@@ -49,6 +49,7 @@ struct PersistArgs {
     int ls[kMaxQueues][kMaxPersistBanks];
     float coef[kMaxRounds][3];   // (a, b, c) of each round
     int claim_early;        // claim the next task while a finished tile's stores drain (set at launch)
+    uint64_t wait_cap;      // constant-clock ticks after which a dependency wait gives up (set at launch)
 };
 
 __host__ __device__ __forceinline__ int sym_count(int tm) { return tm * (tm + 1) / 2; }

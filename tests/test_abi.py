@@ -265,3 +265,11 @@ def test_step_with_slot_scalars_validation(L):
     hp.slot_scalars = 1 << 46
     assert _step(L, [_bank(lr_mul_per_slot=1 << 44)[0]], ws, need, hp) == VALUE
     assert b"lr_mul_per_slot" in L.mb_last_error()
+
+
+def test_persist_fault_hook_validation(L):
+    """The failure-path test hook rejects a negative wait cap and extra queues outside 0..8 (host only)."""
+    assert L.mb_test_persist_faults(-1, 0) == VALUE
+    assert L.mb_test_persist_faults(0, 9) == VALUE
+    assert L.mb_test_persist_faults(0, -1) == VALUE
+    assert L.mb_test_persist_faults(0, 0) == 0
