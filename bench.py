@@ -170,11 +170,12 @@ def main():
     ws = torch.empty(api.mb_step_workspace_bytes(banks), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
-    # ---- one sampled slot stepped on the GPU (compared with the oracle in the CPU-baseline leg;
-    # the full parity checks live in the test suite)
+    # ---- one whole step of every bank on fresh copies of the inputs, in the launch configuration timed
+    # below; the first and last live slot of each bank are compared with the oracle in the CPU-baseline
+    # leg (the full parity checks live in the test suite)
     sample = None
     if not args.no_parity and not args.no_cpu_baseline:
-        sample = gpu_sample_step(api, specs[0], hosts[0])
+        sample = gpu_sample_step(api, specs, upload)
 
     # ---- timed region: K whole steps back to back between two events on the launch stream, nothing
     # else inside it
@@ -371,29 +372,34 @@ def measure_peaks(torch, stream):
                     "(2 GiB of traffic)"}
 
 
-def gpu_sample_step(api, spec, h):
-    """One step of the bank's first live slot on fresh copies of its inputs; the raw output bits."""
+def gpu_sample_step(api, specs, upload):
+    """One whole step of every bank on fresh copies of its inputs (the same banks, workspace size and
+    launches as the timed steps, plus the v_out copy of the Newton-Schulz output); returns, for the first
+    and the last live slot of each bank, the raw output bits."""
     import torch
-    slot = spec.live_slots[0]
-    bf = spec.grad_dtype == "bf16"
-    sl = lambda a: np.ascontiguousarray(a[slot:slot + 1])
-
-    def dev(a, as_bf16=False):
-        t = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
-        return t.view(torch.bfloat16) if as_bf16 and a.dtype == np.uint16 else t
-    b = api.Bank(grad=dev(sl(h["grad"]), bf), momentum=dev(sl(h["momentum"]), bf), w_hi=dev(sl(h["w_hi"])),
-                 w_lo=dev(sl(h["w_lo"])))
-    b.v_out = torch.empty(b.w_hi.shape, dtype=torch.int16, device="cuda")
-    api.muon_bank_step([b])
+    banks = upload()
+    for b in banks:
+        b.v_out = torch.empty(b.w_hi.shape, dtype=torch.int16, device="cuda")
+    ws = torch.empty(api.mb_step_workspace_bytes(banks), dtype=torch.uint8, device="cuda")
+    api.muon_bank_step(banks, workspace=ws)
     torch.cuda.synchronize()
-    mom = (b.momentum.view(torch.int16).cpu().numpy().view(np.uint16) if bf else b.momentum.cpu().numpy())
-    return {"bank": spec.name, "slot": slot, "v": b.v_out.cpu().numpy().view(np.uint16),
-            "w_hi": b.w_hi.cpu().numpy().view(np.uint16), "w_lo": b.w_lo.cpu().numpy().view(np.uint16),
-            "momentum": mom}
+    out = []
+    for spec, b in zip(specs, banks):
+        bf = spec.grad_dtype == "bf16"
+        for slot in dict.fromkeys((spec.live_slots[0], spec.live_slots[-1])):
+            mom = b.momentum[slot:slot + 1]
+            mom = mom.view(torch.int16).cpu().numpy().view(np.uint16) if bf else mom.cpu().numpy()
+            out.append({"bank": spec.name, "slot": slot,
+                        "v": b.v_out[slot:slot + 1].cpu().numpy().view(np.uint16),
+                        "w_hi": b.w_hi[slot:slot + 1].cpu().numpy().view(np.uint16),
+                        "w_lo": b.w_lo[slot:slot + 1].cpu().numpy().view(np.uint16), "momentum": mom})
+    del banks, ws
+    return out
 
 
 def _sample_parity(oracle, spec, h, sample):
-    """The GPU's sampled slot against the oracle's step on the same inputs."""
+    """One slot the GPU stepped against the oracle's step of that slot on the same inputs (every slot of a
+    bank takes the bank's scalars; the oracle's step is per slot)."""
     slot = sample["slot"]
     bf = spec.grad_dtype == "bf16"
     sl = lambda a: np.ascontiguousarray(a[slot:slot + 1])
@@ -413,13 +419,24 @@ def _sample_parity(oracle, spec, h, sample):
             "momentum_bit_exact": ok_mom}
 
 
+def _parity(oracle, specs, hosts, samples):
+    """Every sampled slot against the oracle: the worst Newton-Schulz error and the per-slot results."""
+    by_name = {s.name: (s, h) for s, h in zip(specs, hosts)}
+    checked = [_sample_parity(oracle, *by_name[smp["bank"]], smp) for smp in samples]
+    worst = max(checked, key=lambda c: c["ns_rel_fro_err"])
+    return {"ns_rel_fro_err_max": worst["ns_rel_fro_err"], "worst": {"bank": worst["bank"], "slot": worst["slot"]},
+            "apply_bit_exact": all(c["apply_bit_exact"] for c in checked),
+            "momentum_bit_exact": all(c["momentum_bit_exact"] for c in checked),
+            "tolerance": 3e-2, "slots": checked}
+
+
 def cpu_baseline(specs, hosts, sample=None):
     """The oracle as it stands, on a bounded sample of the same workload, on the host's cores.  With a
-    GPU sample (gpu_sample_step), the oracle's step of that slot is also compared with it; returns
+    GPU sample (gpu_sample_step), the oracle's step of each sampled slot is also compared with it; returns
     (baseline, parity or None)."""
     sys.path.insert(0, HERE)
     import oracle
-    parity = _sample_parity(oracle, specs[0], hosts[0], sample) if sample is not None else None
+    parity = _parity(oracle, specs, hosts, sample) if sample is not None else None
     try:
         from threadpoolctl import threadpool_info
         info = [t for t in threadpool_info() if t.get("user_api") == "blas"]

@@ -41,9 +41,9 @@ def test_flop_count_matches_a_count_of_multiply_adds(m, n):
     assert bench.ns_dense_flops_per_slot(m, n) == bench.ns_dense_flops_per_slot(n, m) == 5 * dense
 
 
-def _oracle_sample(spec, h):
+def _oracle_sample(spec, h, slot=None):
     """A GPU-shaped sample made by the oracle itself: it must pass the comparison."""
-    slot = spec.live_slots[0]
+    slot = spec.live_slots[0] if slot is None else slot
     sl = lambda a: np.ascontiguousarray(a[slot:slot + 1])
     ref = oracle.muon_bank_step(oracle.bf16_bits_to_f64(sl(h["grad"])), oracle.bf16_bits_to_f64(sl(h["momentum"])),
                                 sl(h["w_hi"]), sl(h["w_lo"]), oracle.BF16)
@@ -61,3 +61,22 @@ def test_sample_comparison_accepts_a_correct_step_and_rejects_a_flipped_bit():
     bad["w_lo"].flat[12345] ^= 1
     with pytest.raises(SystemExit):
         bench._sample_parity(oracle, spec, h, bad)
+
+
+def test_parity_over_banks_checks_every_sample_and_reports_the_worst():
+    """The bench samples the first and last live slot of every bank; each is compared with the oracle's
+    step of that slot of its own bank, and one wrong bit anywhere fails the whole check."""
+    specs = WORKLOADS[3][2:]                  # the two gate banks: (16, 1, 12) with one live slot, (16, 6, 12)
+    hosts = [make_bank(3, 2 + i) for i in range(len(specs))]
+    samples = [_oracle_sample(s, h, slot) for s, h in zip(specs, hosts)
+               for slot in dict.fromkeys((s.live_slots[0], s.live_slots[-1]))]
+    assert len(samples) == 3
+    got = bench._parity(oracle, specs, hosts, samples)
+    assert got["apply_bit_exact"] and got["momentum_bit_exact"]
+    assert [(c["bank"], c["slot"]) for c in got["slots"]] == [(s["bank"], s["slot"]) for s in samples]
+    assert got["ns_rel_fro_err_max"] == max(c["ns_rel_fro_err"] for c in got["slots"])
+    bad = [dict(x) for x in samples]
+    bad[-1]["momentum"] = bad[-1]["momentum"].copy()
+    bad[-1]["momentum"].flat[3] ^= 1
+    with pytest.raises(SystemExit):
+        bench._parity(oracle, specs, hosts, bad)
