@@ -386,7 +386,7 @@ def gpu_sample_step(api, specs, upload):
     out = []
     for spec, b in zip(specs, banks):
         bf = spec.grad_dtype == "bf16"
-        for slot in dict.fromkeys((spec.live_slots[0], spec.live_slots[-1])):
+        for slot in dict.fromkeys(spec.live_slots[:1] + spec.live_slots[-1:]):
             mom = b.momentum[slot:slot + 1]
             mom = mom.view(torch.int16).cpu().numpy().view(np.uint16) if bf else mom.cpu().numpy()
             out.append({"bank": spec.name, "slot": slot,
