@@ -1,7 +1,8 @@
 """Planted mistakes in the oracle, each caught by a pin (CPU only).
 
-Every case edits one line of the oracle's source (a dropped term, a transposed operand, a wrong norm, a
-missing round, swapped coefficients, a rounding where the pages slice bits, ...), executes the edited
+Every case edits the oracle's source, one mistake per case (a dropped term, a transposed operand, a wrong norm,
+a missing round, swapped coefficients, a rounding where the pages slice bits, a rounding too many or too few, ...),
+executes the edited
 functions in a copy of the oracle's namespace, binds them where a pin test looks them up, and runs that
 pin: it must fail.  The unedited oracle passes the same pins in tests/test_oracle_*.py.  A case whose
 source line is no longer in the oracle fails too, so an edit of the oracle cannot silently retire a case.
@@ -91,6 +92,32 @@ CASES = [
     ("transpose_add leaves the float32 sum unrounded",
      [("transpose_add", "return round_to_f32(s).astype(np.float32)", "return s")], [],
      {test_oracle_transpose: ["transpose_add"]}, test_oracle_transpose.test_add_f32_is_the_correctly_rounded_sum, ()),
+    ("the apply rounds eta*v before subtracting it",
+     [("mp_apply_update", "prod = eta_b * v", "prod = round_to_f32(eta_b * v)")], [],
+     {test_oracle_apply: ["mp_apply_update"]}, test_oracle_apply.test_apply_is_exactly_rounded_on_random_inputs, ()),
+    ("recombine swaps the two halves",
+     [("recombine", "np.asarray(hi,", "np.asarray(HALF,"), ("recombine", "np.asarray(lo,", "np.asarray(hi,"),
+      ("recombine", "np.asarray(HALF,", "np.asarray(lo,")], ["mp_apply_update"],
+     {test_oracle_apply: ["mp_apply_update"]}, test_oracle_apply.test_apply_identities, ()),
+    ("nu is one minus the rounded mu",
+     [("step_scalars", "nu=_f32(1.0 - momentum),", "nu=_f32(1.0 - _f32(momentum)),")], [],
+     {test_oracle_momentum: ["step_scalars"]}, test_oracle_momentum.test_step_scalars_closed_forms, ()),
+    ("a float32 buffer is stored as bf16",
+     [("momentum_nesterov", "buf_new = _round_sum_of_products(mu, buf, nu, grad, storage)",
+       "buf_new = _round_sum_of_products(mu, buf, nu, grad, BF16)")], [],
+     {test_oracle_momentum: ["momentum_nesterov"]}, test_oracle_momentum.test_momentum_is_exactly_rounded_fp32, ()),
+    ("eps under the square root of the norm",
+     [("frobenius_prescale", "return x / (math.sqrt(float(np.sum(x * x))) + eps)",
+       "return x / math.sqrt(float(np.sum(x * x)) + eps)")], ["newton_schulz"],
+     {test_oracle_ns: ["newton_schulz", "frobenius_prescale"]}, test_oracle_ns.test_ns_equals_svd_closed_form,
+     ((8, 8),)),
+    ("a schedule runs its rounds in reverse",
+     [("newton_schulz", "for (ra, rb, rc) in schedule:", "for (ra, rb, rc) in schedule[::-1]:")], [],
+     {test_oracle_ns: ["newton_schulz"]}, test_oracle_ns.test_schedule_equals_composed_closed_form, ((6, 12),)),
+    ("float32 rounding without gradual underflow",
+     [("round_to_format", "ex = np.maximum(e.astype(np.int64) - 1, emin)", "ex = e.astype(np.int64) - 1")],
+     ["round_to_f32"], {test_oracle_rounding: ["round_to_f32"]}, test_oracle_rounding.test_f32_rounding_matches_numpy_cast,
+     ()),
     ("step reads u from the unrounded buffer",
      [("momentum_nesterov", "u = _round_sum_of_products(nu, grad, mu, buf_new, BF16)",
        "u = _round_sum_of_products(nu, grad, mu, np.asarray(mu) * np.asarray(buf) + np.asarray(nu) * "
