@@ -2,9 +2,8 @@
 
 Every case edits the oracle's source, one mistake per case (a dropped term, a transposed operand, a wrong norm,
 a missing round, swapped coefficients, a rounding where the pages slice bits, a rounding too many or too few, ...),
-executes the edited
-functions in a copy of the oracle's namespace, binds them where a pin test looks them up, and runs that
-pin: it must fail.  The unedited oracle passes the same pins in tests/test_oracle_*.py.  A case whose
+executes the edited functions in a copy of the oracle's namespace, binds them where a pin test looks them up,
+and runs that pin: it must fail.  The unedited oracle passes the same pins in tests/test_oracle_*.py.  A case whose
 source line is no longer in the oracle fails too, so an edit of the oracle cannot silently retire a case.
 
 One plausible mistake is not on the list because no pin can catch it: working on a tall slot without
