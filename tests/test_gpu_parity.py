@@ -47,7 +47,7 @@ def assert_no_wait_fault():
 # apply
 # ---------------------------------------------------------------------------
 
-APPLY_SHAPES = [(3, 64, 64), (2, 37, 11), (1, 1, 12), (5, 128, 200), (40, 768, 768)]
+APPLY_SHAPES = [(3, 64, 64), (2, 37, 11), (1, 1, 12), (5, 128, 200), (40, 768, 768), (3, 1, 1)]
 
 
 @pytest.mark.parametrize("shape", APPLY_SHAPES)
@@ -129,7 +129,9 @@ NS_SHAPES = [(4, 256, 256), (3, 100, 260), (3, 260, 100), (2, 130, 130), (2, 64,
              (2, 1, 12), (3, 6, 12), (2, 12, 6), (2, 768, 768), (1, 3072, 768), (1, 768, 3072), (1, 1024, 1024),
              (1, 200, 8), (2, 257, 129),
              # one workgroup per slot for every round (Gram side <= 64, <= 4096 elements)
-             (16, 1, 12), (16, 6, 12), (2, 64, 64), (3, 40, 3), (2, 16, 256), (2, 256, 16)]
+             (16, 1, 12), (16, 6, 12), (2, 64, 64), (3, 40, 3), (2, 16, 256), (2, 256, 16),
+             # degenerate slots: a scalar, a row and a column of two
+             (3, 1, 1), (2, 1, 2), (2, 2, 1)]
 
 
 @pytest.mark.parametrize("shape", NS_SHAPES)
